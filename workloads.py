@@ -1,0 +1,211 @@
+"""Seeded synthetic workloads for draft branch attention.
+
+This module only draws inputs: sequence lengths, anchor positions, branch
+lengths and N(0,1) tensors, plus the float32 -> bfloat16 round-to-nearest-even
+encoding of those draws. It holds none of the attention arithmetic and none
+of the packing logic, and it serves both the oracle side (tests, CPU
+baseline) and the GPU side (tests, bench) with identical inputs.
+
+Workloads (standing in for the pages' operator benchmarks: EAGLE-3 TTT and
+DFlash/DSpark block drafts at fixed global lengths up to 256K, packed
+variable-length batches; ai.info summary, Main Findings; rainbus analysis,
+Figs. 5 and 6). The RL datasets the pages train on are not used: attention
+consumes projected activations, which are stood in for by N(0,1) draws.
+
+  tiny     1 x 256 tokens, C=2, 2/2 heads, D=64, fp32, TTT depth 3, fwd
+  ttt32k   4 sequences U[4096,12288] summing to 32768, C=4, 32/8/128 bf16,
+           TTT depth 7, fwd
+  dflash   8 sequences summing to 65536 (uniform composition), C=4, 32/8/128
+           bf16, 1024 anchors, bidirectional blocks of 16, fwd+bwd
+  long256k 1 x 262144 tokens, C=8, 32/8/128 bf16, TTT depth 7, fwd+bwd
+  dspark   log-uniform [1024,8192] lengths summing to 131072, C=8, 64/4/128
+           bf16, 2048 anchors, causal blocks of 8 or 16 (p=0.5), fwd+bwd
+
+Reduced variants (suffix ``_r``) keep the head configuration, kind, C and
+structure but shrink the token count so the dense oracle finishes in seconds.
+"""
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+KIND_NONE, KIND_TTT, KIND_BLOCK_BIDIR, KIND_BLOCK_CAUSAL = 0, 1, 2, 3
+KIND_NAMES = {KIND_NONE: "none", KIND_TTT: "ttt", KIND_BLOCK_BIDIR: "block_bidir",
+              KIND_BLOCK_CAUSAL: "block_causal"}
+
+
+@dataclass
+class Workload:
+    name: str
+    seqlens: List[int]
+    C: int
+    r: int
+    kind: int
+    depth_or_block: int
+    hq: int
+    hkv: int
+    d: int
+    dtype: str                      # "bf16" or "fp32"
+    bwd: bool
+    seed: int
+    anchors: Optional[List[int]] = None
+    branch_lens: Optional[List[int]] = None
+    notes: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def n_real(self):
+        return int(sum(self.seqlens))
+
+
+# ---------------------------------------------------------------------------
+# structure generators
+
+
+def lengths_uniform_fixed_total(rng, n, lo, hi, total):
+    """n lengths in [lo, hi] summing to ``total``: draw n-1 uniformly, set the
+    last to the remainder, redraw until it falls in range."""
+    while True:
+        head = rng.integers(lo, hi + 1, size=n - 1)
+        last = total - int(head.sum())
+        if lo <= last <= hi:
+            return [int(x) for x in head] + [last]
+
+
+def lengths_uniform_composition(rng, n, total, quantum=8):
+    """Uniform random composition of ``total`` into n parts: n-1 distinct cut
+    points drawn from the multiples of ``quantum`` strictly inside (0, total)."""
+    cuts = rng.choice(np.arange(quantum, total, quantum), size=n - 1, replace=False)
+    cuts = np.sort(cuts)
+    edges = np.concatenate([[0], cuts, [total]])
+    return [int(x) for x in np.diff(edges)]
+
+
+def lengths_log_uniform(rng, lo, hi, total):
+    """Lengths round(exp(U(ln lo, ln hi))) until the running total reaches
+    ``total``; the last one is truncated to hit the total exactly."""
+    out = []
+    acc = 0
+    while acc < total:
+        x = int(round(float(np.exp(rng.uniform(np.log(lo), np.log(hi))))))
+        x = min(x, total - acc)
+        out.append(x)
+        acc += x
+    return out
+
+
+def anchors_uniform(rng, n_real, n_anchors):
+    """Anchors uniform without replacement over the real tokens of the packed
+    batch, sorted."""
+    return [int(x) for x in np.sort(rng.choice(n_real, size=n_anchors, replace=False))]
+
+
+# ---------------------------------------------------------------------------
+# workloads
+
+
+def make(name):
+    """Build a named workload (structure only; tensors come from ``draw``)."""
+    base = name[:-2] if name.endswith("_r") else name
+    reduced = name.endswith("_r")
+    seed = {"tiny": 1, "ttt32k": 2, "dflash": 3, "long256k": 4, "dspark": 5}[base]
+    rng = np.random.default_rng(seed)
+    if base == "tiny":
+        return Workload(name, [256], 2, 0, KIND_TTT, 3, 2, 2, 64, "fp32", False, seed)
+    if base == "ttt32k":
+        if reduced:
+            lens = lengths_uniform_fixed_total(rng, 4, 300, 1500, 3300)
+        else:
+            lens = lengths_uniform_fixed_total(rng, 4, 4096, 12288, 32768)
+        return Workload(name, lens, 4, 0, KIND_TTT, 7, 32, 8, 128, "bf16", False, seed)
+    if base == "dflash":
+        total, n_anch = (4096, 64) if reduced else (65536, 1024)
+        lens = lengths_uniform_composition(rng, 8, total)
+        anchors = anchors_uniform(rng, total, n_anch)
+        return Workload(name, lens, 4, 0, KIND_BLOCK_BIDIR, 16, 32, 8, 128, "bf16", True,
+                        seed, anchors=anchors)
+    if base == "long256k":
+        n = 2048 if reduced else 262144
+        return Workload(name, [n], 8, 0, KIND_TTT, 7, 32, 8, 128, "bf16", True, seed)
+    if base == "dspark":
+        if reduced:
+            lens = lengths_log_uniform(rng, 64, 512, 3000)
+            n_anch = 96
+        else:
+            lens = lengths_log_uniform(rng, 1024, 8192, 131072)
+            n_anch = 2048
+        total = int(sum(lens))
+        anchors = anchors_uniform(rng, total, n_anch)
+        blens = [int(x) for x in np.where(rng.random(n_anch) < 0.5, 8, 16)]
+        return Workload(name, lens, 8, 0, KIND_BLOCK_CAUSAL, 16, 64, 4, 128, "bf16", True,
+                        seed, anchors=anchors, branch_lens=blens)
+    raise KeyError(name)
+
+
+ALL = ["tiny", "ttt32k", "dflash", "long256k", "dspark"]
+
+
+# ---------------------------------------------------------------------------
+# tensors
+
+
+def f32_to_bf16_bits(x):
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+    Inputs here are finite normal draws, so no NaN handling is needed."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = ((b >> 16) & 1) + np.uint32(0x7FFF)
+    return ((b + rounding) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+TENSOR_ORDER = ["q", "k", "v", "qb", "kb", "vb", "do", "dob"]
+
+
+def tensor_shapes(n_local, n_branch, C, hq, hkv, d):
+    return {
+        "q": (n_local, hq, d), "k": (C, n_local, hkv, d), "v": (C, n_local, hkv, d),
+        "qb": (n_branch, hq, d), "kb": (n_branch, hkv, d), "vb": (n_branch, hkv, d),
+        "do": (n_local, hq, d), "dob": (n_branch, hq, d),
+    }
+
+
+def draw(w, n_local, n_branch, names=TENSOR_ORDER, chunk=1 << 24):
+    """Draw the workload's tensors, N(0,1) float32 in TENSOR_ORDER from one
+    generator seeded by (seed, 1000), then encoded: bf16 workloads return uint16
+    bit patterns, fp32 workloads float32. Tensors not in ``names`` are still
+    drawn (so every tensor's values are independent of which ones are kept)
+    but not returned. ``n_local`` and ``n_branch`` are the row counts of the
+    packed local share and of the local branch rows."""
+    rng = np.random.default_rng([w.seed, 1000])
+    shapes = tensor_shapes(n_local, n_branch, w.C, w.hq, w.hkv, w.d)
+    out = {}
+    for nm in TENSOR_ORDER:
+        if nm in ("do", "dob") and not w.bwd and nm not in names:
+            continue
+        shp = shapes[nm]
+        n = int(np.prod(shp))
+        keep = nm in names
+        if w.dtype == "bf16":
+            buf = np.empty(n, np.uint16) if keep else None
+            for lo in range(0, n, chunk):
+                x = rng.standard_normal(min(chunk, n - lo), dtype=np.float32)
+                if keep:
+                    buf[lo:lo + x.size] = f32_to_bf16_bits(x)
+        else:
+            buf = np.empty(n, np.float32) if keep else None
+            for lo in range(0, n, chunk):
+                x = rng.standard_normal(min(chunk, n - lo), dtype=np.float32)
+                if keep:
+                    buf[lo:lo + x.size] = x
+        if keep:
+            out[nm] = buf.reshape(shp)
+    return out
+
+
+def as_f32(w, arr):
+    """Decode a drawn tensor to float32 values (bf16 bit patterns widened)."""
+    return bf16_bits_to_f32(arr) if w.dtype == "bf16" else np.asarray(arr, np.float32)
