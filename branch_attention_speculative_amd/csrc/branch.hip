@@ -1,0 +1,415 @@
+// Rank-local branch attention (forward partial + Eq. 2 merge, backward) and
+// the backward preprocess Delta = rowsum(dO * O).
+//
+// The branch part is small and stays on the rank that owns the anchor, with
+// no communication (ai.info summary, Key Contributions 1 and Methodology).
+// Each branch row j of an anchor sees that anchor's branch keys j' <= j (TTT
+// chains, causal blocks) or all of them (bidirectional blocks). Its partial
+// (O_b, l_b) is merged with the main-sequence partial (O_m, l_m) produced by
+// the ring kernel using the online-softmax rule (rainbus analysis, core
+// method, Eq. 2): l = log(e^lm + e^lb), O = (e^(lm-l) O_m + e^(lb-l) O_b) /
+// (e^(lm-l) + e^(lb-l)).
+//
+// These kernels run on the vector ALUs: a branch holds at most 64 keys, so
+// the work is tiny next to the ring part. Templated on element type (bf16
+// bits or float), head dim and the longest branch of the plan.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ba {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T *p, int64_t i);
+template <>
+__device__ __forceinline__ float ldf<u16>(const u16 *p, int64_t i) {
+  return bf2f(p[i]);
+}
+template <>
+__device__ __forceinline__ float ldf<float>(const float *p, int64_t i) {
+  return p[i];
+}
+
+// load 8 consecutive elements as floats (16-byte aligned for bf16, 32 for fp32)
+template <typename T>
+__device__ __forceinline__ void ld8(const T *p, int64_t i, float (&o)[8]);
+template <>
+__device__ __forceinline__ void ld8<u16>(const u16 *p, int64_t i, float (&o)[8]) {
+  const u32x4 x = *reinterpret_cast<const u32x4 *>(p + i);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(x[k] << 16);
+    o[2 * k + 1] = __uint_as_float(x[k] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void ld8<float>(const float *p, int64_t i, float (&o)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p + i);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + i + 4);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = a[k];
+    o[4 + k] = b[k];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void st8(T *p, int64_t i, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void st8<u16>(u16 *p, int64_t i, const float (&v)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = pack_bf2(v[2 * k], v[2 * k + 1]);
+  *reinterpret_cast<u32x4 *>(p + i) = w;
+}
+template <>
+__device__ __forceinline__ void st8<float>(float *p, int64_t i, const float (&v)[8]) {
+  *reinterpret_cast<f32x4 *>(p + i) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4 *>(p + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// Stage the branch keys/values of a tile (rows [base, base + rows), kv-head g)
+// in LDS as floats, row-major [row][DIM].
+template <typename T, int DIM>
+__device__ __forceinline__ void stage_branch_kv(const T *KB, const T *VB, int base, int rows,
+                                                int g, int hkv, float *sK, float *sV) {
+  for (int id = threadIdx.x; id < rows * (DIM / 8); id += blockDim.x) {
+    const int rr = id / (DIM / 8), dc = id % (DIM / 8);
+    const int64_t off = (int64_t(base + rr) * hkv + g) * DIM + dc * 8;
+    float k8[8], v8[8];
+    ld8<T>(KB, off, k8);
+    ld8<T>(VB, off, v8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sK[rr * DIM + dc * 8 + e] = k8[e];
+      sV[rr * DIM + dc * 8 + e] = v8[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+template <typename T, int DIM, int MAXB>
+__global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
+  __shared__ float sK[kMaxBranch * DIM];
+  __shared__ float sV[kMaxBranch * DIM];
+  const BTile t = a.btiles[blockIdx.x];
+  if (t.rows == 0) return;
+  const int base = a.branch_off[t.a0];
+  const int G = a.G;
+  const T *QB = static_cast<const T *>(a.qb);
+  stage_branch_kv<T, DIM>(static_cast<const T *>(a.kb), static_cast<const T *>(a.vb), base, t.rows,
+                          t.g, a.hkv, sK, sV);
+  __syncthreads();
+  for (int qv = threadIdx.x; qv < t.rows * G; qv += blockDim.x) {
+    const int row = base + qv / G;
+    const int h = t.g * G + qv % G;
+    const int an = a.b_anchor[row];
+    const int lo = a.branch_off[an];
+    const int n = a.branch_off[an + 1] - lo;
+    const int j = row - lo;
+    const int nvis = a.bidir ? n : j + 1;
+    const int kl0 = lo - base;
+    const int64_t qh = int64_t(row) * a.hq + h;
+    float s[MAXB];
+#pragma unroll
+    for (int jj = 0; jj < MAXB; ++jj) s[jj] = 0.f;
+    for (int dc = 0; dc < DIM / 8; ++dc) {
+      float q8[8];
+      ld8<T>(QB, qh * DIM + dc * 8, q8);
+#pragma unroll
+      for (int jj = 0; jj < MAXB; ++jj) {
+        if (jj < nvis) {
+          const float *kr = sK + (kl0 + jj) * DIM + dc * 8;
+          float acc = s[jj];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fmaf(q8[e], kr[e], acc);
+          s[jj] = acc;
+        }
+      }
+    }
+    // branch partial: max and sum in the log2 domain
+    float mb = kNegInf;
+#pragma unroll
+    for (int jj = 0; jj < MAXB; ++jj)
+      if (jj < nvis) {
+        s[jj] *= a.scale_log2;
+        mb = fmaxf(mb, s[jj]);
+      }
+    float lsum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < MAXB; ++jj) {
+      s[jj] = jj < nvis ? fast_exp2(s[jj] - mb) : 0.f;
+      lsum += s[jj];
+    }
+    const float lb2 = mb + log2f(lsum);  // branch-local LSE (log2)
+    const float lm2 = a.lm[qh] * kLog2e;   // main-sequence LSE (log2)
+    // Eq. 2: l = log(e^lm + e^lb); weights e^(lm - l), e^(lb - l)
+    const float hi = fmaxf(lm2, lb2);
+    const float l2 = hi + log2f(fast_exp2(lm2 - hi) + fast_exp2(lb2 - hi));
+    const float wm = fast_exp2(lm2 - l2);
+    const float wb = fast_exp2(lb2 - l2);
+    const float norm = 1.f / (wm + wb);
+    const float cm = wm * norm, cb = wb * norm / lsum;
+    T *OB = static_cast<T *>(a.ob);
+    for (int dc = 0; dc < DIM / 8; ++dc) {
+      float o8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[e] = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < MAXB; ++jj) {
+        if (jj < nvis) {
+          const float *vr = sV + (kl0 + jj) * DIM + dc * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o8[e] = fmaf(s[jj], vr[e], o8[e]);
+        }
+      }
+      float m8[8];
+      ld8<float>(a.om, qh * DIM + dc * 8, m8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[e] = cm * m8[e] + cb * o8[e];
+      st8<T>(OB, qh * DIM + dc * 8, o8);
+    }
+    a.lseb[qh] = l2 * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+template <typename T, int DIM>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
+  // 16 lanes per (row, head); rows are main rows then branch rows
+  const int64_t pair = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const int64_t total = (int64_t(a.n_local) + a.n_branch) * a.hq;
+  float acc = 0.f;
+  bool pad = true;
+  if (pair < total) {
+    const int64_t row = pair / a.hq;
+    const bool main = row < a.n_local;
+    pad = main && a.bound_main[row] < 0;
+    const int64_t qh = main ? pair : pair - int64_t(a.n_local) * a.hq;
+    const T *O = static_cast<const T *>(main ? a.o : a.ob);
+    const T *DO = static_cast<const T *>(main ? a.dout : a.doutb);
+    constexpr int PER = DIM / 16;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int64_t i = qh * DIM + sub * PER + e;
+      acc = fmaf(ldf<T>(O, i), ldf<T>(DO, i), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 8, 16);
+  acc += __shfl_xor(acc, 4, 16);
+  acc += __shfl_xor(acc, 2, 16);
+  acc += __shfl_xor(acc, 1, 16);
+  if (pair < total && sub == 0) a.delta[pair] = pad ? 0.f : acc;
+}
+
+// ---------------------------------------------------------------------------
+
+constexpr int kBQ = 128;  // query vectors per backward chunk
+
+template <typename T, int DIM, int MAXB>
+__global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
+  __shared__ float sK[kMaxBranch * DIM];
+  __shared__ float sV[kMaxBranch * DIM];
+  __shared__ float sP[kBQ * kMaxBranch];
+  __shared__ float sS[kBQ * kMaxBranch];
+  const BTile t = a.btiles[blockIdx.x];
+  if (t.rows == 0) return;
+  const int base = a.branch_off[t.a0];
+  const int G = a.G;
+  const int tid = threadIdx.x;
+  const T *QB = static_cast<const T *>(a.qb);
+  const T *DOB = static_cast<const T *>(a.doutb);
+  stage_branch_kv<T, DIM>(static_cast<const T *>(a.kb), static_cast<const T *>(a.vb), base, t.rows,
+                          t.g, a.hkv, sK, sV);
+  // phase-2 items: (key row kl, 4 consecutive d) -> fixed per thread
+  constexpr int ITEMS = (kMaxBranch * DIM / 4 + 255) / 256;
+  float adk[ITEMS][4], adv[ITEMS][4];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) adk[it][e] = adv[it][e] = 0.f;
+  const int nqv = t.rows * G;
+  for (int c0 = 0; c0 < nqv; c0 += kBQ) {
+    const int nq = min(kBQ, nqv - c0);
+    __syncthreads();  // staged K/V visible; previous chunk's sP/sS reads done
+    if (tid < nq) {
+      const int qv = c0 + tid;
+      const int row = base + qv / G;
+      const int h = t.g * G + qv % G;
+      const int an = a.b_anchor[row];
+      const int lo = a.branch_off[an];
+      const int n = a.branch_off[an + 1] - lo;
+      const int j = row - lo;
+      const int nvis = a.bidir ? n : j + 1;
+      const int kl0 = lo - base;
+      const int64_t qh = int64_t(row) * a.hq + h;
+      float s[MAXB], dp[MAXB];
+#pragma unroll
+      for (int jj = 0; jj < MAXB; ++jj) s[jj] = dp[jj] = 0.f;
+      for (int dc = 0; dc < DIM / 8; ++dc) {
+        float q8[8], d8[8];
+        ld8<T>(QB, qh * DIM + dc * 8, q8);
+        ld8<T>(DOB, qh * DIM + dc * 8, d8);
+#pragma unroll
+        for (int jj = 0; jj < MAXB; ++jj) {
+          if (jj < nvis) {
+            const float *kr = sK + (kl0 + jj) * DIM + dc * 8;
+            const float *vr = sV + (kl0 + jj) * DIM + dc * 8;
+            float as = s[jj], ad = dp[jj];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              as = fmaf(q8[e], kr[e], as);
+              ad = fmaf(d8[e], vr[e], ad);
+            }
+            s[jj] = as;
+            dp[jj] = ad;
+          }
+        }
+      }
+      const float lse2 = a.lseb[qh] * kLog2e;
+      const float del = a.delta_b[qh];
+      for (int kl = 0; kl < t.rows; ++kl) {
+        sP[tid * kMaxBranch + kl] = 0.f;
+        sS[tid * kMaxBranch + kl] = 0.f;
+      }
+#pragma unroll
+      for (int jj = 0; jj < MAXB; ++jj) {
+        if (jj < nvis) {
+          const float p = fast_exp2(s[jj] * a.scale_log2 - lse2);
+          const float d = p * (dp[jj] - del);
+          s[jj] = d;  // keep dS for the dQ sum
+          sP[tid * kMaxBranch + kl0 + jj] = p;
+          sS[tid * kMaxBranch + kl0 + jj] = d;
+        } else {
+          s[jj] = 0.f;
+        }
+      }
+      for (int dc = 0; dc < DIM / 8; ++dc) {
+        float o8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < MAXB; ++jj) {
+          if (jj < nvis) {
+            const float *kr = sK + (kl0 + jj) * DIM + dc * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = fmaf(s[jj], kr[e], o8[e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] *= a.scale;
+        st8<float>(a.dq_local, qh * DIM + dc * 8, o8);
+      }
+    }
+    __syncthreads();
+    // phase 2: dK[kl] += scale * sum_q dS[q][kl] Q[q]; dV[kl] += sum_q P[q][kl] dO[q]
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int item = tid + 256 * it;
+      if (item < t.rows * (DIM / 4)) {
+        const int kl = item / (DIM / 4), d4 = item % (DIM / 4);
+        const int an = a.b_anchor[base + kl];
+        const int lo = a.branch_off[an] - base;
+        const int hi = a.branch_off[an + 1] - base;
+        const int q_lo = max(lo * G, c0), q_hi = min(hi * G, c0 + nq);
+        for (int qv = q_lo; qv < q_hi; ++qv) {
+          const float p = sP[(qv - c0) * kMaxBranch + kl];
+          const float d = sS[(qv - c0) * kMaxBranch + kl];
+          if (p == 0.f && d == 0.f) continue;
+          const int row = base + qv / G;
+          const int h = t.g * G + qv % G;
+          const int64_t off = (int64_t(row) * a.hq + h) * DIM + d4 * 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            adk[it][e] = fmaf(d, ldf<T>(QB, off + e), adk[it][e]);
+            adv[it][e] = fmaf(p, ldf<T>(DOB, off + e), adv[it][e]);
+          }
+        }
+      }
+    }
+  }
+  T *DKB = static_cast<T *>(a.dkb);
+  T *DVB = static_cast<T *>(a.dvb);
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int item = tid + 256 * it;
+    if (item < t.rows * (DIM / 4)) {
+      const int kl = item / (DIM / 4), d4 = item % (DIM / 4);
+      const int64_t off = (int64_t(base + kl) * a.hkv + t.g) * DIM + d4 * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(T) == 2) {
+          DKB[off + e] = f2bf(adk[it][e] * a.scale);
+          DVB[off + e] = f2bf(adv[it][e]);
+        } else {
+          DKB[off + e] = adk[it][e] * a.scale;
+          DVB[off + e] = adv[it][e];
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int DIM>
+hipError_t fwd_branch_dispatch(const FwdBranchArgs &a, int n, int maxb, hipStream_t s) {
+  if (maxb <= 8)
+    hipLaunchKernelGGL((fwd_branch_kernel<T, DIM, 8>), dim3(n), dim3(256), 0, s, a);
+  else if (maxb <= 16)
+    hipLaunchKernelGGL((fwd_branch_kernel<T, DIM, 16>), dim3(n), dim3(256), 0, s, a);
+  else if (maxb <= 32)
+    hipLaunchKernelGGL((fwd_branch_kernel<T, DIM, 32>), dim3(n), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_branch_kernel<T, DIM, 64>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DIM>
+hipError_t bwd_branch_dispatch(const BwdBranchArgs &a, int n, int maxb, hipStream_t s) {
+  if (maxb <= 8)
+    hipLaunchKernelGGL((bwd_branch_kernel<T, DIM, 8>), dim3(n), dim3(256), 0, s, a);
+  else if (maxb <= 16)
+    hipLaunchKernelGGL((bwd_branch_kernel<T, DIM, 16>), dim3(n), dim3(256), 0, s, a);
+  else if (maxb <= 32)
+    hipLaunchKernelGGL((bwd_branch_kernel<T, DIM, 32>), dim3(n), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_branch_kernel<T, DIM, 64>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_branch(const FwdBranchArgs &a, int n_tiles, int dtype, int maxb,
+                             hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  if (dtype == BA_BF16) return fwd_branch_dispatch<u16, 128>(a, n_tiles, maxb, s);
+  if (a.d == 64) return fwd_branch_dispatch<float, 64>(a, n_tiles, maxb, s);
+  return fwd_branch_dispatch<float, 128>(a, n_tiles, maxb, s);
+}
+
+hipError_t launch_bwd_pre(const BwdPreArgs &a, int dtype, hipStream_t s) {
+  const int64_t total = (int64_t(a.n_local) + a.n_branch) * a.hq;
+  const int64_t blocks = (total + 15) / 16;
+  if (blocks <= 0) return hipSuccess;
+  if (dtype == BA_BF16)
+    hipLaunchKernelGGL((bwd_pre_kernel<u16, 128>), dim3(blocks), dim3(256), 0, s, a);
+  else if (a.d == 64)
+    hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_branch(const BwdBranchArgs &a, int n_tiles, int dtype, int maxb,
+                             hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  if (dtype == BA_BF16) return bwd_branch_dispatch<u16, 128>(a, n_tiles, maxb, s);
+  if (a.d == 64) return bwd_branch_dispatch<float, 64>(a, n_tiles, maxb, s);
+  return bwd_branch_dispatch<float, 128>(a, n_tiles, maxb, s);
+}
+
+}  // namespace ba

@@ -1,0 +1,232 @@
+/*
+ * branch_attn.h -- C ABI of the MI355X (gfx950) draft branch attention library.
+ *
+ * What it computes (pages of arXiv:2609.07108):
+ *   ai.info summary, Key Contributions 1 and Methodology: draft branch
+ *   attention is split into a causal main-sequence part, evaluated by packed,
+ *   load-balanced zigzag ring attention (K/V circulate, queries stay), and a
+ *   rank-local branch part on the rank that owns the branch's anchor; the two
+ *   (O, LSE) partials are merged with the online-softmax rule, which equals the
+ *   full attention.
+ *   rainbus analysis, core method, Eq. 2: l = log(e^lm + e^lb),
+ *   O = (e^(lm-l) Om + e^(lb-l) Ob) / (e^(lm-l) + e^(lb-l)).
+ *   rainbus analysis, method steps, steps two and five: ring steps over the C
+ *   ranks' K/V shards forward; the backward replays the ring and accumulates
+ *   gradients locally.
+ *
+ * On one GPU the library computes ONE context-parallel rank's share at its
+ * real shape: rank r's local zigzag rows (main rows and the branch rows of the
+ * anchors it owns) against every virtual ring step's K/V shard, all resident
+ * in device memory. No inter-GPU traffic happens here.
+ *
+ * Visible key set of a query row (the definition the kernels reproduce):
+ *   real main row at position p of sequence s  -> main keys of s at 0..p;
+ *   branch row j of an anchor at position pa   -> main keys of s at 0..pa, plus
+ *       the anchor's branch keys j' <= j (TTT chains, causal blocks) or all of
+ *       them (bidirectional blocks);
+ *   pad row -> nothing (O = 0, LSE = -inf); pad keys are never visible.
+ * For q-head h the kv-head is h / (hq / hkv). Scores are scale * <q, k>; LSE
+ * is the natural log-sum-exp of the scores.
+ *
+ * Zigzag layout: every sequence is padded at its tail to a multiple of 2C and
+ * cut into 2C equal chunks; rank r holds chunk r then chunk 2C-1-r, sequences
+ * in batch order. "Local rows" of rank r are those chunks, back to back.
+ *
+ * Tensor layouts (all contiguous, row-major, element type = dtype unless
+ * stated; N = n_local_rows, NB = n_branch_rows):
+ *   q, o, dq, do            [N,  hq,  d]
+ *   k, v, dk, dv            [C,  N,   hkv, d]  shard s = rank s's local rows
+ *   qb, ob, dqb, dob        [NB, hq,  d]       branch rows of the local anchors,
+ *                                              anchor after anchor (branch_off)
+ *   kb, vb, dkb, dvb        [NB, hkv, d]       one branch key per branch row
+ *   lse                     [N,  hq]  float32
+ *   lseb                    [NB, hq]  float32
+ * dk/dv hold this rank's contribution to the gradient of every shard (in a
+ * real ring they travel back to their owners); dq/dk/dv of pad rows are 0.
+ *
+ * Ownership and threading:
+ *   - The caller owns every device buffer and the stream. A plan is created
+ *     on the host (ba_plan_create), uploaded once to the current device
+ *     (ba_plan_upload: the only call that allocates device memory), and is
+ *     immutable afterwards, so concurrent use on several streams is safe.
+ *   - branch_attn_fwd / branch_attn_bwd never allocate and never synchronise:
+ *     they validate, then enqueue kernels on the caller's stream and return.
+ *     Asynchronous device faults surface at the caller's next synchronisation.
+ *   - Pointers must be device pointers, 16-byte aligned.
+ * Errors: every entry point returns a ba_status; no C++ exception crosses the
+ * ABI and nothing is printed. ba_last_error() gives a thread-local detail
+ * string for the last failing call on that thread.
+ */
+#ifndef BRANCH_ATTN_H
+#define BRANCH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BA_OK = 0,
+  BA_E_INVALID = 1,     /* bad argument (sizes, order, pointers, state) */
+  BA_E_UNSUPPORTED = 2, /* valid but outside what this build supports */
+  BA_E_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  BA_E_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  BA_E_OOM = 5          /* host or device allocation failed */
+} ba_status;
+
+typedef enum { BA_BF16 = 0, BA_FP32 = 1 } ba_dtype;
+
+typedef enum {
+  BA_BRANCH_NONE = 0,         /* main rows only: plain causal zigzag ring attention */
+  BA_BRANCH_TTT = 1,          /* EAGLE-3 training-time test: every real position anchors
+                                 depth_or_block chained rows; row j sees branch keys 0..j
+                                 (paperlens walkthrough, "The two walls") */
+  BA_BRANCH_BLOCK_BIDIR = 2,  /* DFlash: a block branch, bidirectional inside the block */
+  BA_BRANCH_BLOCK_CAUSAL = 3  /* DSpark: a block branch, causal inside the block (rainbus
+                                 analysis, background on the three draft families) */
+} ba_branch_kind;
+
+typedef struct ba_plan ba_plan; /* opaque, library-owned */
+
+/* Sizes and work counts of a plan (all counts per rank). */
+typedef struct {
+  int32_t n_seqs, cp_degree, cp_rank, kind, hq, hkv, d, dtype;
+  int32_t max_branch_len;
+  int32_t reserved;
+  int64_t n_local_rows;    /* N: rank-local main rows, pads included */
+  int64_t n_pad_rows;      /* pad rows among them */
+  int64_t n_local_anchors; /* anchors owned by this rank */
+  int64_t n_branch_rows;   /* NB */
+  int64_t pairs_main;      /* unmasked (row, key) pairs per q-head: main rows */
+  int64_t pairs_prefix;    /* branch rows x main prefix keys */
+  int64_t pairs_local;     /* branch rows x own branch keys */
+  int64_t pairs_total;
+  size_t ws_fwd_bytes;     /* device workspace branch_attn_fwd needs */
+  size_t ws_bwd_bytes;     /* device workspace branch_attn_bwd needs */
+} ba_plan_info;
+
+/* Host index arrays of a plan (library-owned, valid until ba_plan_destroy). */
+typedef struct {
+  const int32_t *cu_real;    /* [n_seqs+1] prefix sums of real lengths */
+  const int32_t *cu_pad;     /* [n_seqs+1] prefix sums of padded lengths */
+  const int32_t *cu_local;   /* [n_seqs+1] prefix sums of local rows (2 chunks each) */
+  const int32_t *perm;       /* [N] local row -> global padded position cu_pad[s]+pos */
+  const int32_t *is_pad;     /* [N] 1 for pad rows */
+  const int32_t *pos;        /* [N] position inside its sequence */
+  const int32_t *seq;        /* [N] sequence id */
+  const int32_t *anchor_row; /* [A] local main row of each local anchor */
+  const int32_t *anchor_pos; /* [A] its position inside the sequence */
+  const int32_t *anchor_seq; /* [A] its sequence */
+  const int32_t *branch_off; /* [A+1] first branch row of each local anchor */
+} ba_indices;
+
+/*
+ * Build the plan of rank cp_rank of cp_degree (host only, no device calls).
+ *   seqlens[n_seqs]   real lengths, in packed order, each >= 1.
+ *   kind              see ba_branch_kind.
+ *   depth_or_block    TTT: chain depth (rows per anchor, >= 1); block kinds:
+ *                     uniform block length when branch_lens is NULL.
+ *   anchors[n_anchors] block kinds only: global indices into the packed stream
+ *                     of real tokens, strictly increasing (NULL/0 otherwise).
+ *   branch_lens       block kinds: per-anchor block length (NULL = uniform).
+ *   hq, hkv, d, dtype head configuration the plan's work lists are built for.
+ * Supported: hq % hkv == 0 with hq/hkv a power of two <= 64; bf16 needs d == 128,
+ * fp32 takes d == 64 or 128; branch lengths 1..64.
+ * Returns BA_E_INVALID / BA_E_UNSUPPORTED with *out untouched on error.
+ * Partition rule: rainbus analysis, background on context parallelism (head
+ * and tail chunk per rank) and method steps, step two (N/C tokens per rank).
+ */
+ba_status ba_plan_create(const int32_t *seqlens, int32_t n_seqs, int32_t cp_degree,
+                         int32_t cp_rank, ba_branch_kind kind, int32_t depth_or_block,
+                         const int32_t *anchors, int32_t n_anchors,
+                         const int32_t *branch_lens, int32_t hq, int32_t hkv, int32_t d,
+                         ba_dtype dtype, ba_plan **out);
+
+/* Copy the plan's index arrays and work lists to the CURRENT HIP device
+ * (hipMalloc + synchronous copies). Must precede fwd/bwd; calling it again on
+ * the same device is a no-op, on another device BA_E_INVALID. */
+ba_status ba_plan_upload(ba_plan *plan);
+
+ba_status ba_plan_get_info(const ba_plan *plan, ba_plan_info *out);
+ba_status ba_plan_get_indices(const ba_plan *plan, ba_indices *out);
+void ba_plan_destroy(ba_plan *plan); /* frees host and device memory; NULL is a no-op */
+
+/*
+ * Inspection of the kernels' work lists (host copies, library-owned, valid
+ * until ba_plan_destroy). which = 0: query tiles of the forward and dQ
+ * kernels, 8 int32 each {kv_head, source (0 main rows, 1 branch rows), first
+ * row, rows, first local row of the sequence, chunk size, smallest causal
+ * bound, largest causal bound}; which = 1: key tiles of the dK/dV kernel, 12
+ * int32 each {kv_head, shard, first key row in the shard, its position, keys,
+ * first/end main row, first/end branch row, sequence, 0, 0}; which = 2:
+ * branch tiles, 4 int32 each {kv_head, first anchor, end anchor, rows}.
+ * Tiles with zero rows/keys are padding slots. Order = launch order.
+ */
+ba_status ba_plan_get_worklist(const ba_plan *plan, int32_t which, const int32_t **data,
+                               int64_t *n_tiles, int32_t *ints_per_tile);
+
+typedef struct {
+  float scale;                 /* softmax scale; <= 0 means 1/sqrt(d) */
+  const void *q, *k, *v;       /* inputs, layouts above */
+  const void *qb, *kb, *vb;    /* branch inputs; may be NULL when NB == 0 */
+  void *o;                     /* [N, hq, d] */
+  float *lse;                  /* [N, hq] */
+  void *ob;                    /* [NB, hq, d]; NULL when NB == 0 */
+  float *lseb;                 /* [NB, hq];    NULL when NB == 0 */
+  void *workspace;             /* device scratch of >= ws_fwd_bytes (may be NULL if 0) */
+  size_t workspace_bytes;
+} ba_fwd_args;
+
+typedef struct {
+  float scale;                 /* same scale as the forward */
+  const void *q, *k, *v, *qb, *kb, *vb;
+  const void *o, *ob;          /* forward outputs */
+  const float *lse, *lseb;     /* forward LSEs (the merged ones) */
+  const void *dout, *doutb;    /* incoming gradients of o and ob */
+  void *dq, *dk, *dv;          /* [N,hq,d], [C,N,hkv,d], [C,N,hkv,d]; fully overwritten */
+  void *dqb, *dkb, *dvb;       /* [NB,hq,d], [NB,hkv,d], [NB,hkv,d]; fully overwritten */
+  void *workspace;             /* device scratch of >= ws_bwd_bytes */
+  size_t workspace_bytes;
+} ba_bwd_args;
+
+/*
+ * Forward: main-sequence partial over every ring step i = 0..C-1 (shard
+ * (r - i) mod C, merged in registers between steps), the rank-local branch
+ * partial, and the Eq. 2 merge of the two for every branch row.
+ * stream: a hipStream_t (NULL = default stream). Enqueue only.
+ */
+ba_status branch_attn_fwd(const ba_plan *plan, const ba_fwd_args *args, void *stream);
+
+/*
+ * Backward, recomputed from the merged LSE: Delta = rowsum(dO * O), then the
+ * ring replay (dQ for every local row; dK/dV for every shard), the branch-local
+ * backward, and the final sums. Enqueue only.
+ */
+ba_status branch_attn_bwd(const ba_plan *plan, const ba_bwd_args *args, void *stream);
+
+const char *ba_status_str(ba_status s);
+const char *ba_last_error(void);
+
+/*
+ * Kernel timing (measurement aid; off by default). While enabled, every kernel
+ * launch of fwd/bwd is bracketed by HIP events recorded on the launch stream.
+ * ba_profile_read synchronises those events and returns, per kernel name, the
+ * number of launches and their summed duration in milliseconds, then resets.
+ * Event creation happens in ba_profile_enable, never inside fwd/bwd.
+ */
+typedef struct {
+  char name[32];
+  int64_t launches;
+  double total_ms;
+} ba_kernel_time;
+
+ba_status ba_profile_enable(int32_t on, int32_t max_launches);
+ba_status ba_profile_read(ba_kernel_time *out, int32_t max_entries, int32_t *n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BRANCH_ATTN_H */

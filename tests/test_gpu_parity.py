@@ -1,0 +1,266 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle,
+element by element on the same seeded inputs.
+
+Tolerances (stated once, used everywhere):
+  forward, bf16 inputs: max |O - O_ref| <= 2e-2 and rel-L2(O) <= 1e-2,
+                        max |LSE - LSE_ref| <= 1e-3;
+  forward, fp32 inputs: max |O - O_ref| <= 1e-5, max |LSE - LSE_ref| <= 1e-5;
+  gradients, bf16: max-abs <= 2e-2 * max(1, |ref|_inf) and rel-L2 <= 1e-2;
+  gradients, fp32: max-abs <= 1e-4 * max(1, |ref|_inf).
+The rel-L2 guard on O matters at long context, where |O| itself shrinks
+towards 2e-2 and a max-abs bound alone would accept O = 0.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attn, pack
+
+from helpers import LazyF32, grad_ok, inputs, lse_err, make_plan, max_abs, oracle_structs, \
+    rel_l2, say, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import branch_attention_speculative_amd as ba
+    ba.lib()
+    return torch, ba
+
+
+def _run(env, w, with_bwd, oracle_dtype=np.float32):
+    torch, ba = env
+    say(f"[case] {w.name}: lens={w.seqlens[:6]}{'...' if len(w.seqlens) > 6 else ''} C={w.C} r={w.r} "
+        f"kind={w.kind} depth/block={w.depth_or_block} heads={w.hq}/{w.hkv} d={w.d} {w.dtype}")
+    lay, br = oracle_structs(w)
+    plan = make_plan(ba, w)
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    assert (N, NB) == (lay["n_local"], br["n_branch"])
+    raw, dec = inputs(w, N, NB)
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    o, lse, ob, lseb = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+    res = dict(o=o, lse=lse, ob=ob, lseb=lseb)
+    if with_bwd:
+        g = ba.bwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"], o, lse, ob,
+                   lseb, dev["do"], dev["dob"])
+        res.update(zip(("dq", "dk", "dv", "dqb", "dkb", "dvb"), g))
+    torch.cuda.synchronize()
+    got = {k: to_host(v) for k, v in res.items()}
+    ins = [dec[k] for k in ("q", "k", "v", "qb", "kb", "vb")]
+    ref = dict(zip(("o", "lse", "ob", "lseb"), attn.attn_fwd(lay, br, *ins, dtype=oracle_dtype)))
+    if with_bwd:
+        ref.update(zip(("dq", "dk", "dv", "dqb", "dkb", "dvb"),
+                       attn.attn_bwd(lay, br, *ins, dec["do"], dec["dob"], dtype=oracle_dtype)))
+    return got, ref, plan
+
+
+def _check_fwd(w, got, ref):
+    bf16 = w.dtype == "bf16"
+    for o_name, l_name in (("o", "lse"), ("ob", "lseb")):
+        if ref[o_name].size == 0:
+            continue
+        e_o = max_abs(got[o_name], ref[o_name])
+        e_l = lse_err(got[l_name], ref[l_name])
+        r_o = rel_l2(got[o_name], ref[o_name])
+        say(f"  {o_name}: max|dO|={e_o:.3e} relL2={r_o:.3e}  {l_name}: max|dLSE|={e_l:.3e}")
+        if bf16:
+            assert e_o <= 2e-2 and r_o <= 1e-2, (o_name, e_o, r_o)
+            assert e_l <= 1e-3, (l_name, e_l)
+        else:
+            assert e_o <= 1e-5, (o_name, e_o)
+            assert e_l <= 1e-5, (l_name, e_l)
+
+
+def _check_bwd(w, got, ref):
+    for name in ("dq", "dk", "dv", "dqb", "dkb", "dvb"):
+        ok, ma, rl = grad_ok(got[name], ref[name], w.dtype == "bf16")
+        say(f"  {name}: max-abs={ma:.3e} relL2={rl:.3e} |ref|inf={np.max(np.abs(ref[name])) if ref[name].size else 0:.3e}")
+        assert ok, (name, ma, rl)
+
+
+# ---------------------------------------------------------------------------
+# full parity at sizes the oracle finishes in seconds
+
+
+def test_tiny_fp32_forward(env):
+    # the tiny EAGLE-3 TTT workload in full: 256 tokens, C=2, fp32, depth 3
+    w = workloads.make("tiny")
+    got, ref, _ = _run(env, w, with_bwd=False, oracle_dtype=np.float64)
+    _check_fwd(w, got, ref)
+
+
+@pytest.mark.parametrize("kind,d,C", [(pack.KIND_TTT, 64, 3), (pack.KIND_BLOCK_BIDIR, 128, 2),
+                                      (pack.KIND_BLOCK_CAUSAL, 64, 4), (pack.KIND_NONE, 128, 1)])
+def test_fp32_forward_backward(env, kind, d, C):
+    rng = np.random.default_rng(kind * 10 + C)
+    lens = [37, 5, 70]
+    n_real = sum(lens)
+    anchors = blens = None
+    depth = 3
+    if kind in (pack.KIND_BLOCK_BIDIR, pack.KIND_BLOCK_CAUSAL):
+        anchors = [0, 4, 36, 37, 41, 60, 111]
+        blens = [int(x) for x in rng.integers(1, 9, size=len(anchors))]
+        depth = 0
+    if kind == pack.KIND_NONE:
+        depth = 0
+    w = workloads.Workload(f"fp32-k{kind}", lens, C, C - 1, kind, depth, 4, 2, d, "fp32", True,
+                           77 + kind, anchors=anchors, branch_lens=blens)
+    got, ref, _ = _run(env, w, with_bwd=True, oracle_dtype=np.float64)
+    _check_fwd(w, got, ref)
+    _check_bwd(w, got, ref)
+
+
+@pytest.mark.parametrize("name", ["ttt32k_r", "dflash_r", "long256k_r", "dspark_r"])
+def test_reduced_workloads(env, name):
+    w = workloads.make(name)
+    got, ref, _ = _run(env, w, with_bwd=w.bwd or name == "ttt32k_r")
+    _check_fwd(w, got, ref)
+    if "dq" in got:
+        _check_bwd(w, got, ref)
+
+
+def _edge(name, lens, C, r, kind, depth, hq, hkv, anchors=None, blens=None):
+    seed = sum(ord(ch) for ch in name)
+    return workloads.Workload(name, lens, C, r, kind, depth, hq, hkv, 128, "bf16", True,
+                              seed, anchors=anchors, branch_lens=blens)
+
+
+EDGES = [
+    # plain causal ring attention, C=1, one-token and odd-length sequences
+    _edge("none-c1", [1, 2, 3, 130], 1, 0, pack.KIND_NONE, 0, 4, 2),
+    # sequences shorter than 2C: pad rows inside the head chunk, empty shards
+    _edge("short-c8", [5, 3, 17, 1], 8, 5, pack.KIND_TTT, 2, 8, 2),
+    # anchors on the first and last real tokens, blocks of 1 and of 64
+    _edge("block-edges", [40, 200], 2, 1, pack.KIND_BLOCK_BIDIR, 0, 16, 4,
+          anchors=[0, 39, 40, 150, 239], blens=[1, 64, 5, 64, 1]),
+    _edge("block-edges-causal", [40, 200], 2, 0, pack.KIND_BLOCK_CAUSAL, 0, 16, 4,
+          anchors=[0, 39, 40, 150, 239], blens=[1, 64, 5, 64, 1]),
+    # multi-head attention (G=1) and wide groups (G=16, G=64)
+    _edge("mha", [300], 2, 1, pack.KIND_TTT, 3, 2, 2),
+    _edge("g16", [257, 100], 4, 2, pack.KIND_BLOCK_CAUSAL, 0, 16, 1,
+          anchors=[3, 100, 256, 300], blens=[8, 16, 8, 16]),
+    _edge("g64", [129], 2, 0, pack.KIND_TTT, 1, 64, 1),
+    # block kind with no anchors at all on this rank
+    _edge("block-empty", [64, 64], 4, 3, pack.KIND_BLOCK_BIDIR, 16, 8, 2, anchors=[0], blens=[4]),
+    # a long single chunk: several key blocks per shard, ragged tails
+    _edge("ragged", [1999], 3, 1, pack.KIND_TTT, 2, 8, 2),
+]
+
+
+@pytest.mark.parametrize("w", EDGES, ids=[e.name for e in EDGES])
+def test_edge_cases(env, w):
+    got, ref, _ = _run(env, w, with_bwd=True)
+    _check_fwd(w, got, ref)
+    _check_bwd(w, got, ref)
+
+
+def test_forward_is_deterministic_and_stream_ordered(env):
+    torch, ba = env
+    w = workloads.make("dflash_r")
+    plan = make_plan(ba, w)
+    raw, _ = inputs(w, plan.info["n_local_rows"], plan.info["n_branch_rows"],
+                    names=["q", "k", "v", "qb", "kb", "vb"])
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+        b = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+    s.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled rows against the row-wise oracle, plus the
+# gradient sum rules that hold at any size
+
+
+def _sample_rows(lay, br, rng, n_main, n_anchor):
+    """First and last two rows of both local chunks of the first and last
+    sequence, plus seeded random rows; all branch rows of the first, the last
+    and a few random local anchors."""
+    rows = set()
+    S = lay["L"].size
+    for s in sorted({0, S - 1}):
+        c = int(lay["c"][s])
+        for half in range(2):
+            lo = int(lay["cu_local"][s]) + half * c
+            rows |= {lo, lo + min(1, c - 1), lo + c - 1, lo + max(c - 2, 0)}
+    rows |= set(rng.choice(lay["n_local"], size=n_main, replace=False).tolist())
+    A = br["anchor_row"].size
+    brows = []
+    if A:
+        pick = {0, A - 1} | set(rng.choice(A, size=min(n_anchor, A), replace=False).tolist())
+        for a in sorted(pick):
+            brows += list(range(int(br["branch_off"][a]), int(br["branch_off"][a + 1])))
+    return sorted(rows), brows
+
+
+@pytest.mark.parametrize("name", ["ttt32k", "dflash", "dspark", "long256k"])
+def test_full_size_sampled(env, name):
+    torch, ba = env
+    w = workloads.make(name)
+    say(f"[case] full-size {name}")
+    lay, br = oracle_structs(w)
+    plan = make_plan(ba, w)
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    raw = workloads.draw(w, N, NB)
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    o, lse, ob, lseb = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+    grads = None
+    if w.bwd:
+        grads = ba.bwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"], o, lse,
+                       ob, lseb, dev["do"], dev["dob"])
+    torch.cuda.synchronize()
+    say("  device pass done")
+    rng = np.random.default_rng(7)
+    rows, brows = _sample_rows(lay, br, rng, n_main=12, n_anchor=3)
+    L = {k: LazyF32(w, v) for k, v in raw.items()}
+    ref = attn.attn_rows(lay, br, L["q"], L["k"], L["v"], L["qb"], L["kb"], L["vb"], rows, brows,
+                         dtype=np.float32, do=L["do"] if w.bwd else None,
+                         dob=L["dob"] if w.bwd else None)
+    say(f"  oracle rows done ({len(rows)} main, {len(brows)} branch)")
+    ri = torch.tensor(rows, device="cuda")
+    bi = torch.tensor(brows, device="cuda", dtype=torch.long)
+    g_o, g_l = to_host(o[ri]), to_host(lse[ri])
+    w_o = np.stack([ref["main"][r]["o"] for r in rows])
+    w_l = np.stack([ref["main"][r]["lse"] for r in rows])
+    checks = [("o", g_o, w_o, g_l, w_l)]
+    if brows:
+        checks.append(("ob", to_host(ob[bi]), np.stack([ref["branch"][r]["o"] for r in brows]),
+                       to_host(lseb[bi]), np.stack([ref["branch"][r]["lse"] for r in brows])))
+    for nm, go, wo, gl, wl in checks:
+        e_o, r_o, e_l = max_abs(go, wo), rel_l2(go, wo), lse_err(gl, wl)
+        say(f"  {nm}: max|dO|={e_o:.3e} relL2={r_o:.3e} max|dLSE|={e_l:.3e}")
+        assert e_o <= 2e-2 and r_o <= 1e-2 and e_l <= 1e-3
+    if grads is None:
+        return
+    dq, dk, dv, dqb, dkb, dvb = grads
+    gq = to_host(dq[ri])
+    wq = np.stack([ref["main"][r]["dq"] for r in rows])
+    ok, ma, rl = grad_ok(gq, wq, True)
+    say(f"  dq: max-abs={ma:.3e} relL2={rl:.3e}")
+    assert ok
+    if brows:
+        ok, ma, rl = grad_ok(to_host(dqb[bi]), np.stack([ref["branch"][r]["dq"] for r in brows]), True)
+        say(f"  dqb: max-abs={ma:.3e} relL2={rl:.3e}")
+        assert ok
+    # sum rules per kv-group: sum_k dV_k = sum_q dO_q (real rows), sum_k dK_k = 0
+    G = w.hq // w.hkv
+    real = torch.tensor(lay["is_pad"] == 0, device="cuda")
+    do_sum = dev["do"].float()[real].view(-1, w.hkv, G, w.d).sum(dim=(0, 2))
+    if NB:
+        do_sum += dev["dob"].float().view(NB, w.hkv, G, w.d).sum(dim=(0, 2))
+    dv_sum = dv.float().sum(dim=(0, 1)) + (dvb.float().sum(dim=0) if NB else 0)
+    dk_sum = dk.float().sum(dim=(0, 1)) + (dkb.float().sum(dim=0) if NB else 0)
+    dv_mag = dv.float().abs().sum(dim=(0, 1)) + (dvb.float().abs().sum(dim=0) if NB else 0)
+    dk_mag = dk.float().abs().sum(dim=(0, 1)) + (dkb.float().abs().sum(dim=0) if NB else 0)
+    ev = float(((dv_sum - do_sum).abs() / dv_mag.clamp_min(1e-6)).max())
+    ek = float((dk_sum.abs() / dk_mag.clamp_min(1e-6)).max())
+    say(f"  sum rules: |sum dV - sum dO|/sum|dV| = {ev:.3e}, |sum dK|/sum|dK| = {ek:.3e}")
+    assert ev <= 1e-2 and ek <= 1e-2

@@ -173,37 +173,40 @@ def tensor_shapes(n_local, n_branch, C, hq, hkv, d):
     }
 
 
-def draw(w, n_local, n_branch, names=TENSOR_ORDER, chunk=1 << 24):
-    """Draw the workload's tensors, N(0,1) float32 in TENSOR_ORDER from one
-    generator seeded by (seed, 1000), then encoded: bf16 workloads return uint16
-    bit patterns, fp32 workloads float32. Tensors not in ``names`` are still
-    drawn (so every tensor's values are independent of which ones are kept)
-    but not returned. ``n_local`` and ``n_branch`` are the row counts of the
-    packed local share and of the local branch rows."""
-    rng = np.random.default_rng([w.seed, 1000])
+def _fill(w, tensor_id, shape, lo, n, out, chunk):
+    rng = np.random.default_rng([w.seed, 1000 + tensor_id, lo // chunk])
+    x = rng.standard_normal(n, dtype=np.float32)
+    if w.dtype == "bf16":
+        out[lo:lo + n] = f32_to_bf16_bits(x)
+    else:
+        out[lo:lo + n] = x
+
+
+def draw(w, n_local, n_branch, names=TENSOR_ORDER, chunk=1 << 22, threads=None):
+    """Draw the workload's tensors: N(0,1) float32, encoded as bf16 bit
+    patterns (uint16) for bf16 workloads or kept float32. Element block b of
+    tensor t (blocks of ``chunk`` elements) comes from its own generator seeded
+    by (seed, 1000 + t, b), so the values do not depend on which tensors are
+    requested or on how many threads draw them. ``n_local`` and ``n_branch``
+    are the row counts of the packed local share and of the local branch rows."""
+    import concurrent.futures
+    import os
     shapes = tensor_shapes(n_local, n_branch, w.C, w.hq, w.hkv, w.d)
     out = {}
-    for nm in TENSOR_ORDER:
-        if nm in ("do", "dob") and not w.bwd and nm not in names:
+    jobs = []
+    for t, nm in enumerate(TENSOR_ORDER):
+        if nm not in names:
             continue
         shp = shapes[nm]
         n = int(np.prod(shp))
-        keep = nm in names
-        if w.dtype == "bf16":
-            buf = np.empty(n, np.uint16) if keep else None
-            for lo in range(0, n, chunk):
-                x = rng.standard_normal(min(chunk, n - lo), dtype=np.float32)
-                if keep:
-                    buf[lo:lo + x.size] = f32_to_bf16_bits(x)
-        else:
-            buf = np.empty(n, np.float32) if keep else None
-            for lo in range(0, n, chunk):
-                x = rng.standard_normal(min(chunk, n - lo), dtype=np.float32)
-                if keep:
-                    buf[lo:lo + x.size] = x
-        if keep:
-            out[nm] = buf.reshape(shp)
-    return out
+        buf = np.empty(n, np.uint16 if w.dtype == "bf16" else np.float32)
+        out[nm] = buf
+        for lo in range(0, n, chunk):
+            jobs.append((t, shp, lo, min(chunk, n - lo), buf))
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda j: _fill(w, j[0], j[1], j[2], j[3], j[4], chunk), jobs))
+    return {nm: out[nm].reshape(shapes[nm]) for nm in out}
 
 
 def as_f32(w, arr):
