@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark: draft branch attention fwd+bwd on one MI355X.
+
+One step = one full pass of the hot path over one synthetic batch: the
+forward (ring-step causal partial over every virtual ring step, branch-local
+partial, Eq. 2 merge) and the backward (Delta, branch-local backward, dQ and
+dK/dV ring replay). Inputs are resident in device memory before timing.
+
+Throughput is effective TFLOP/s over unmasked (query row, key) pairs only:
+4*D FLOP per pair per q-head forward (Q K^T and P V), 10*D backward
+(recomputed Q K^T, dO V^T, dV, dQ, dK). Pads are excluded.
+
+Prints one JSON line. Default workload: one 262,144-token sequence at virtual
+CP=8, rank 0's share (32,768 local rows, 229,376 EAGLE-3 TTT branch rows of
+depth 7), 32 q-heads / 8 kv-heads, d=128, bf16.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096)
+PEAK_HBM_GBS = 8000.0
+METRIC = "branch-attn fwd+bwd effective TFLOP/s (1 GPU) and % of bf16 MFMA peak"
+
+# algorithmic FLOP per unmasked pair per q-head and per unit of D, per kernel:
+# the forward ring kernel does Q K^T and P V over the main keys; the dK/dV
+# kernel does the four backward contractions over the main keys (Q K^T
+# recompute, dO V^T, P^T dO, dS^T Q); the dQ kernel is credited only dS K
+# (its Q K^T and dO V^T recomputes are not counted).
+KERNEL_FLOP_PER_PAIR_D = {"fwd_ring": 4, "bwd_dkdv": 8, "bwd_dq": 2}
+KERNEL_SOURCES = {"fwd_ring": ["fwd_ring.hip", "common.h"],
+                  "bwd_dkdv": ["bwd_ring.hip", "common.h"],
+                  "bwd_dq": ["bwd_ring.hip", "common.h"]}
+
+
+def describe(w, info):
+    kind = {0: "no branches", 1: f"EAGLE-3 TTT depth {w.depth_or_block}",
+            2: "DFlash bidirectional blocks", 3: "DSpark causal blocks"}[w.kind]
+    return (f"{w.name}: {len(w.seqlens)} seq / {sum(w.seqlens)} tokens, virtual CP={w.C} rank {w.r} "
+            f"share ({info['n_local_rows']} local rows, {info['n_branch_rows']} branch rows), "
+            f"{w.hq}/{w.hkv} heads, d={w.d}, {w.dtype}, {kind}, fwd+bwd")
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "branch_attention_speculative_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, used
+    only if the kernel sources still hash to the value recorded there."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_h = re.search(r"source_hash:\s*([0-9a-f]+)", txt)
+    if not (m_b and m_h) or m_h.group(1) != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, plan_info, raw, n_anchor_sample, seed=11):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the main row and every branch row of ``n_anchor_sample`` seeded anchors,
+    forward and backward (their dQ and their dK/dV contributions), against
+    their full visible key sets."""
+    from threadpoolctl import threadpool_info
+    from oracle import attn, pack
+
+    class Lazy:
+        def __init__(self, a):
+            self.a, self.shape = a, a.shape
+
+        def __getitem__(self, idx):
+            return workloads.as_f32(w, self.a[idx])
+
+    lay = pack.zigzag_layout(w.seqlens, w.C, w.r)
+    if w.kind == pack.KIND_TTT:
+        br = pack.branch_index(lay, w.kind, w.depth_or_block)
+    elif w.kind == pack.KIND_NONE:
+        br = pack.branch_index(lay, w.kind)
+    else:
+        br = pack.branch_index(lay, w.kind, w.depth_or_block, w.anchors, w.branch_lens)
+    rng = np.random.default_rng(seed)
+    A = br["anchor_row"].size
+    pick = np.sort(rng.choice(A, size=min(n_anchor_sample, A), replace=False))
+    main_rows = br["anchor_row"][pick].tolist()
+    branch_rows = [b for a in pick for b in range(br["branch_off"][a], br["branch_off"][a + 1])]
+    L = {k: Lazy(v) for k, v in raw.items()}
+    dk_acc, dv_acc = {}, {}
+    t0 = time.perf_counter()
+    attn.attn_rows(lay, br, L["q"], L["k"], L["v"], L["qb"], L["kb"], L["vb"], main_rows,
+                   branch_rows, dtype=np.float32, do=L["do"], dob=L["dob"], dk_acc=dk_acc,
+                   dv_acc=dv_acc)
+    dt = time.perf_counter() - t0
+    # unmasked pairs of the sampled rows, from the visibility rules
+    pairs = int(np.sum(lay["pos"][main_rows] + 1))
+    for b in branch_rows:
+        a = br["b_anchor"][b]
+        n = br["branch_off"][a + 1] - br["branch_off"][a]
+        own = n if br["kind"] == pack.KIND_BLOCK_BIDIR else br["b_j"][b] + 1
+        pairs += int(br["anchor_pos"][a]) + 1 + int(own)
+    flop = pairs * w.hq * w.d * 14
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    total_pairs = plan_info["pairs_total"]
+    return {
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"{len(main_rows)} anchors of the same workload: their {len(main_rows)} main rows "
+                   f"+ {len(branch_rows)} branch rows x {w.hq} heads, fwd+bwd against full key sets "
+                   f"({pairs} of {total_pairs} pairs per head, {dt:.1f} s, fp32 NumPy)"),
+        "seconds": dt, "extrapolated_step_s": dt * total_pairs / max(pairs, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="long256k", choices=workloads.ALL)
+    ap.add_argument("--cpu-anchors", type=int, default=12,
+                    help="anchors in the CPU-oracle sample (0 skips the CPU baseline)")
+    ap.add_argument("--no-profile", action="store_true", help="skip per-kernel event timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU ring is not part of this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import branch_attention_speculative_amd as ba
+    if not os.path.exists(ba.LIB_PATH):
+        from branch_attention_speculative_amd import build as _b
+        _b.build()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w = workloads.make(args.workload)
+    plan = ba.Plan(w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.anchors, w.branch_lens,
+                   w.hq, w.hkv, w.d, w.dtype).upload()
+    info = plan.info
+    N, NB = info["n_local_rows"], info["n_branch_rows"]
+    print(f"[bench] {describe(w, info)}", file=sys.stderr, flush=True)
+    raw = workloads.draw(w, N, NB)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    T = {k: dev(v) for k, v in raw.items()}
+    del tdt
+    ws_f = torch.empty(max(info["ws_fwd_bytes"], 1), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(max(info["ws_bwd_bytes"], 1), dtype=torch.uint8, device="cuda")
+    print("[bench] inputs resident", file=sys.stderr, flush=True)
+
+    def step():
+        o, lse, ob, lseb = ba.fwd(plan, T["q"], T["k"], T["v"], T["qb"], T["kb"], T["vb"],
+                                  workspace=ws_f)
+        return ba.bwd(plan, T["q"], T["k"], T["v"], T["qb"], T["kb"], T["vb"], o, lse, ob, lseb,
+                      T["do"], T["dob"], workspace=ws_b)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+
+    if not args.no_profile:
+        ba.profile_enable(True, max_launches=16 * args.steps + 16)
+        ba.profile_read()  # reset
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    kern = ba.profile_read() if not args.no_profile else {}
+    if not args.no_profile:
+        ba.profile_enable(False)
+    print(f"[bench] timed {args.steps} steps: {ms:.2f} ms/step (wall {wall:.2f} s)", file=sys.stderr,
+          flush=True)
+
+    pairs = info["pairs_total"]
+    pairs_main_keys = info["pairs_main"] + info["pairs_prefix"]
+    flop_step = pairs * w.hq * w.d * (4 + 10)
+    tflops = flop_step / (ms * 1e-3) / 1e12
+    kernels = {}
+    for name, (n, tot) in kern.items():
+        avg = tot / max(n, 1)
+        entry = {"launches_per_step": n / args.steps, "avg_ms": avg, "share": tot / (ms * args.steps)}
+        if name in KERNEL_FLOP_PER_PAIR_D:
+            f = KERNEL_FLOP_PER_PAIR_D[name] * w.d * pairs_main_keys * w.hq
+            entry["algorithmic_tflop_per_launch"] = f / 1e12
+            entry["achieved_tflops"] = f / (avg * 1e-3) / 1e12
+        kernels[name] = entry
+    roof = None
+    if kernels:
+        dom = max((k for k in kernels if k in KERNEL_FLOP_PER_PAIR_D),
+                  key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
+        ach = kernels[dom]["achieved_tflops"]
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                "traffic": read_traffic(dom, w.name)}
+    cpu = None
+    if args.cpu_anchors > 0:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, info, raw, args.cpu_anchors)
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {"workload": describe(w, info), "tokens": int(sum(w.seqlens)),
+                   "cp_degree": w.C, "cp_rank": w.r, "local_rows": N, "branch_rows": NB,
+                   "pairs_per_head": pairs, "flop_per_step": flop_step},
+        "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "wall_s": wall,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
