@@ -11,9 +11,14 @@
 // tiles each see a suffix of the sequence's main rows and of its branch rows
 // (query rows and anchors are stored in increasing position order, so the
 // rows whose causal bound reaches a key form a suffix).
+//
+// Both kernels keep their streamed tiles (K/V, resp. Q/dO) double-buffered
+// in LDS in row-major form, load the next tile into registers while the
+// current one is computed, and read the operands that are contracted over
+// rows (K^T for dQ; Q^T and dO^T for dK/dV) with the LDS transpose read.
 
-#include "common.h"
 #include "kernels.h"
+#include "ring_common.h"
 
 namespace ba {
 
@@ -21,91 +26,12 @@ namespace {
 
 constexpr int kBN = 64;  // keys per block in the dQ kernel
 
-struct Seg {
-  int n_hi, n_full, cpos0;
-  int64_t krow;
-};
-
-__device__ __forceinline__ Seg seg_info(int sg, const QTile &t, int C, int r, int n_local) {
-  const int i = sg >> 1, half = sg & 1;
-  int sh = r - i;
-  if (sh < 0) sh += C;
-  const int chunk = half ? 2 * C - 1 - sh : sh;
-  Seg s;
-  s.cpos0 = chunk * t.c;
-  s.n_hi = min(max(t.p_max - s.cpos0 + 1, 0), t.c);
-  s.n_full = min(max(t.p_min - s.cpos0 + 1, 0), t.c);
-  s.krow = int64_t(sh) * n_local + t.seq_off + int64_t(half) * t.c;
-  return s;
-}
-
-__device__ __forceinline__ void next_block(int &sg, int &j0, Seg &s, const QTile &t, int C, int r,
-                                           int n_local) {
-  j0 += kBN;
-  if (j0 < s.n_hi) return;
-  j0 = 0;
-  for (++sg; sg < 2 * C; ++sg) {
-    s = seg_info(sg, t, C, r, n_local);
-    if (s.n_hi > 0) return;
-  }
-}
-
-__device__ __forceinline__ void first_block(int &sg, int &j0, Seg &s, const QTile &t, int C, int r,
-                                            int n_local) {
-  j0 = 0;
-  for (sg = 0; sg < 2 * C; ++sg) {
-    s = seg_info(sg, t, C, r, n_local);
-    if (s.n_hi > 0) return;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // dQ: query-stationary ring replay
 
-struct DqRegs {
-  u32x4 k[4], v[4];  // natural K and V rows: 4 x 16 B each per thread
-  u32x2 kt[8];       // K for the transposed store: 8 keys x 4 d
-};
-
-__device__ __forceinline__ void dq_load(DqRegs &R, const u16 *__restrict__ K,
-                                        const u16 *__restrict__ V, const Seg &s, int j0, int g,
-                                        int hkv, int tid) {
-  const int64_t rs = int64_t(hkv) * 128;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + 256 * i;
-    const int key = id >> 4, dc = id & 15;
-    const int64_t off = (s.krow + min(j0 + key, s.n_hi - 1)) * rs + g * 128 + dc * 8;
-    R.k[i] = *reinterpret_cast<const u32x4 *>(K + off);
-    R.v[i] = *reinterpret_cast<const u32x4 *>(V + off);
-  }
-  const int dgrp = tid & 31, kgrp = tid >> 5;
-  const int u = kgrp >> 1, sub = kgrp & 1;
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int key = 16 * u + kslot16(8 * sub + jj);
-    R.kt[jj] = *reinterpret_cast<const u32x2 *>(K + (s.krow + min(j0 + key, s.n_hi - 1)) * rs +
-                                                 g * 128 + 4 * dgrp);
-  }
-}
-
-__device__ __forceinline__ void dq_store(const DqRegs &R, u16 *sK, u16 *sV, u16 *sKt, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + 256 * i;
-    const int key = id >> 4, dc = id & 15;
-    *reinterpret_cast<u32x4 *>(sK + key * kNatStride + dc * 8) = R.k[i];
-    *reinterpret_cast<u32x4 *>(sV + key * kNatStride + dc * 8) = R.v[i];
-  }
-  const int dgrp = tid & 31, kgrp = tid >> 5;
-  const int u = kgrp >> 1, sub = kgrp & 1;
-  store_t8x4(R.kt, sKt + (4 * dgrp) * kTrStride + 16 * u + 8 * sub, kTrStride);
-}
-
-__global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdDqArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sK[kBN * kNatStride];
-  __shared__ __attribute__((aligned(16))) u16 sV[kBN * kNatStride];
-  __shared__ __attribute__((aligned(16))) u16 sKt[128 * kTrStride];
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 sK[2][kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sV[2][kBN * kRS];
 
   const QTile t = a.qtiles[blockIdx.x];
   if (t.nrows == 0) return;
@@ -140,66 +66,70 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdDqArgs a) {
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  const float sl2 = a.scale_log2;
+  const float c = a.scale_log2;
 
   int sg, j0;
   Seg s;
-  first_block(sg, j0, s, t, a.C, a.r, a.n_local);
-  DqRegs R;
-  if (sg < 2 * a.C) dq_load(R, K, V, s, j0, t.g, a.hkv, tid);
-
-  while (sg < 2 * a.C) {
+  first_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+  const int nseg = 2 * a.C;
+  u32x4 RK[4], RV[4];
+  if (sg < nseg) {
+    load_rows64(RK, K, s, j0, t.g, a.hkv, tid);
+    load_rows64(RV, V, s, j0, t.g, a.hkv, tid);
+    store_rows64(RK, sK[0], tid);
+    store_rows64(RV, sV[0], tid);
+  }
+  __syncthreads();
+  int cur = 0;
+  while (sg < nseg) {
     const Seg cs = s;
     const int cj0 = j0;
-    next_block(sg, j0, s, t, a.C, a.r, a.n_local);
-    __syncthreads();
-    dq_store(R, sK, sV, sKt, tid);
-    __syncthreads();
-    if (sg < 2 * a.C) dq_load(R, K, V, s, j0, t.g, a.hkv, tid);
-    if (!wave_active) continue;
-
-    // S^T = K Q^T and dP^T = V dO^T for 64 keys
-    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int o0 = qi * kNatStride + ks * 16 + hf * 8;
-      const int o1 = (32 + qi) * kNatStride + ks * 16 + hf * 8;
-      s0 = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sK + o0)), qreg[ks], s0);
-      s1 = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sK + o1)), qreg[ks], s1);
-      p0 = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sV + o0)), dreg[ks], p0);
-      p1 = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sV + o1)), dreg[ks], p1);
+    next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+    const bool more = sg < nseg;
+    if (more) {
+      load_rows64(RK, K, s, j0, t.g, a.hkv, tid);
+      load_rows64(RV, V, s, j0, t.g, a.hkv, tid);
     }
-    const bool need_mask = cj0 + kBN > cs.n_full;
-    float ds[32];
+    if (wave_active) {
+      const u16 *bk = sK[cur];
+      const u16 *bv = sV[cur];
+      // S^T = K Q^T and dP^T = V dO^T for 64 keys
+      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
 #pragma unroll
-    for (int v = 0; v < 32; ++v) {
-      const float sv = v < 16 ? s0[v] : s1[v - 16];
-      const float dpv = v < 16 ? p0[v] : p1[v - 16];
-      float p = fast_exp2(sv * sl2 - lse2);
-      if (need_mask) {
-        const int jj = cj0 + 32 * (v >> 4) + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
-        const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
-        p = vis ? p : 0.f;
+      for (int ks = 0; ks < 8; ++ks) {
+        s0 = mfma32(lds_nat(bk, 0, ks * 16, lane), qreg[ks], s0);
+        s1 = mfma32(lds_nat(bk, 32, ks * 16, lane), qreg[ks], s1);
+        p0 = mfma32(lds_nat(bv, 0, ks * 16, lane), dreg[ks], p0);
+        p1 = mfma32(lds_nat(bv, 32, ks * 16, lane), dreg[ks], p1);
       }
-      ds[v] = p * (dpv - delta);
-    }
-    bf16x8 db[4];
+      const bool need_mask = cj0 + kBN > cs.n_full;
+      float ds[32];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      u32x4 w;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) w[p] = pack_bf2(ds[8 * u + 2 * p], ds[8 * u + 2 * p + 1]);
-      db[u] = as_bf16x8(w);
-    }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int v = 0; v < 32; ++v) {
+        const float sv = v < 16 ? s0[v] : s1[v - 16];
+        const float dpv = v < 16 ? p0[v] : p1[v - 16];
+        float p = fast_exp2(fmaf(sv, c, -lse2));
+        if (need_mask) {
+          const int jj = cj0 + 32 * (v >> 4) + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
+          const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
+          p = vis ? p : 0.f;
+        }
+        ds[v] = p * (dpv - delta);
+      }
+      // dQ^T += K^T dS^T
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8 ak = as_bf16x8(
-            *reinterpret_cast<const u32x4 *>(sKt + (32 * dt + qi) * kTrStride + 16 * u + 8 * hf));
-        acc[dt] = mfma32(ak, db[u], acc[dt]);
+        const bf16x8 db = pack8(ds + 8 * u);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma32(lds_tr(bk, 16 * u, 32 * dt, lane), db, acc[dt]);
       }
+    }
+    if (more) {
+      store_rows64(RK, sK[cur ^ 1], tid);
+      store_rows64(RV, sV[cur ^ 1], tid);
+    }
+    __syncthreads();
+    cur ^= 1;
   }
 
   if (!valid) return;
@@ -220,8 +150,8 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdDqArgs a) {
         x3 += l[3];
       }
       u32x2 w;
-      w.x = pack_bf2(x0, x1);
-      w.y = pack_bf2(x2, x3);
+      w.x = cvt_pk_bf16(x0, x1);
+      w.y = cvt_pk_bf16(x2, x3);
       *reinterpret_cast<u32x2 *>(DQ + qh * 128 + d0) = w;
     }
 }
@@ -231,14 +161,85 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdDqArgs a) {
 
 constexpr int kQB = 64;  // query vectors per inner block
 
+struct QBlockRegs {
+  u32x4 q[4], d[4];
+  float l, del;
+  int b;
+};
+
+// Inner blocks are numbered over the main-row range then the branch-row range.
+struct QBlock {
+  int src, r0, nr;
+};
+
+__device__ __forceinline__ QBlock qblock(const KTile &t, int b, int RB, int nb_main) {
+  QBlock q;
+  if (b < nb_main) {
+    q.src = 0;
+    q.r0 = t.qm_start + b * RB;
+    q.nr = min(RB, t.qm_end - q.r0);
+  } else {
+    q.src = 1;
+    q.r0 = t.qb_start + (b - nb_main) * RB;
+    q.nr = min(RB, t.qb_end - q.r0);
+  }
+  return q;
+}
+
+__device__ __forceinline__ void qblock_load(QBlockRegs &R, const BwdDkdvArgs &a, const KTile &t,
+                                            const QBlock &qb, int tid) {
+  const u16 *Q = static_cast<const u16 *>(qb.src ? a.qb : a.q);
+  const u16 *DO = static_cast<const u16 *>(qb.src ? a.doutb : a.dout);
+  const int G = a.G, log2G = a.log2G;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + 256 * i;
+    const int mq = id >> 4, dc = id & 15;
+    const int rl = mq >> log2G;
+    R.q[i] = u32x4{0, 0, 0, 0};
+    R.d[i] = u32x4{0, 0, 0, 0};
+    if (rl < qb.nr) {
+      const int64_t off = (int64_t(qb.r0 + rl) * a.hq + t.g * G + (mq & (G - 1))) * 128 + dc * 8;
+      R.q[i] = *reinterpret_cast<const u32x4 *>(Q + off);
+      R.d[i] = *reinterpret_cast<const u32x4 *>(DO + off);
+    }
+  }
+  if (tid < kQB) {
+    const int rl = tid >> log2G;
+    R.l = 0.f;
+    R.del = 0.f;
+    R.b = -1;
+    if (rl < qb.nr) {
+      const int64_t qh = int64_t(qb.r0 + rl) * a.hq + t.g * G + (tid & (G - 1));
+      R.l = (qb.src ? a.lseb : a.lse)[qh] * kLog2e;
+      R.del = a.delta[(qb.src ? int64_t(a.n_local) * a.hq : 0) + qh];
+      R.b = (qb.src ? a.bound_branch : a.bound_main)[qb.r0 + rl];
+    }
+  }
+}
+
+__device__ __forceinline__ void qblock_store(const QBlockRegs &R, u16 *sQ, u16 *sD, float *sL,
+                                             float *sDel, int *sB, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + 256 * i;
+    const int mq = id >> 4, dc = id & 15;
+    *reinterpret_cast<u32x4 *>(sQ + mq * kRS + dc * 8) = R.q[i];
+    *reinterpret_cast<u32x4 *>(sD + mq * kRS + dc * 8) = R.d[i];
+  }
+  if (tid < kQB) {
+    sL[tid] = R.l;
+    sDel[tid] = R.del;
+    sB[tid] = R.b;
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sQ[kQB * kNatStride];
-  __shared__ __attribute__((aligned(16))) u16 sD[kQB * kNatStride];
-  __shared__ __attribute__((aligned(16))) u16 sQt[128 * kTrStride];
-  __shared__ __attribute__((aligned(16))) u16 sDt[128 * kTrStride];
-  __shared__ __attribute__((aligned(16))) float sL[kQB];
-  __shared__ __attribute__((aligned(16))) float sDel[kQB];
-  __shared__ __attribute__((aligned(16))) int sB[kQB];
+  __shared__ __attribute__((aligned(16))) u16 sQ[2][kQB * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sD[2][kQB * kRS];
+  __shared__ __attribute__((aligned(16))) float sL[2][kQB];
+  __shared__ __attribute__((aligned(16))) float sDel[2][kQB];
+  __shared__ __attribute__((aligned(16))) int sB[2][kQB];
 
   const KTile t = a.ktiles[blockIdx.x];
   if (t.nkeys == 0) return;
@@ -247,7 +248,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   const int kk = wave * 32 + qi;  // this lane's key inside the tile
   const bool kvalid = kk < t.nkeys;
   const int kpos = t.kpos0 + kk;
-  const int G = a.G, log2G = a.log2G;
   const int64_t krow = int64_t(t.shard) * a.n_local + t.krow0 + min(kk, t.nkeys - 1);
   const int64_t koff = (krow * a.hkv + t.g) * 128;
   const u16 *K = static_cast<const u16 *>(a.k);
@@ -265,132 +265,76 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     adk[dt] = f32x16{};
     adv[dt] = f32x16{};
   }
-  const float sl2 = a.scale_log2;
-  const int RB = kQB >> log2G;  // rows per inner block
+  const float c = a.scale_log2;
+  const int RB = kQB >> a.log2G;  // rows per inner block
   const bool wave_active = (wave * 32) < t.nkeys;
+  const int nb_main = (t.qm_end - t.qm_start + RB - 1) / RB;
+  const int nb = nb_main + (t.qb_end - t.qb_start + RB - 1) / RB;
 
-  for (int src = 0; src < 2; ++src) {
-    const int lo = src ? t.qb_start : t.qm_start;
-    const int hi = src ? t.qb_end : t.qm_end;
-    const u16 *Q = static_cast<const u16 *>(src ? a.qb : a.q);
-    const u16 *DO = static_cast<const u16 *>(src ? a.doutb : a.dout);
-    const float *LSE = src ? a.lseb : a.lse;
-    const int32_t *BOUND = src ? a.bound_branch : a.bound_main;
-    const float *DEL = a.delta + (src ? int64_t(a.n_local) * a.hq : 0);
-    for (int r0 = lo; r0 < hi; r0 += RB) {
-      const int nr = min(RB, hi - r0);
-      __syncthreads();  // previous block's LDS reads are done
-      // natural Q / dO tiles
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int id = tid + 256 * i;
-        const int mq = id >> 4, dc = id & 15;
-        const int rl = mq >> log2G;
-        u32x4 xq = {0, 0, 0, 0}, xd = {0, 0, 0, 0};
-        if (rl < nr) {
-          const int64_t off = (int64_t(r0 + rl) * a.hq + t.g * G + (mq & (G - 1))) * 128 + dc * 8;
-          xq = *reinterpret_cast<const u32x4 *>(Q + off);
-          xd = *reinterpret_cast<const u32x4 *>(DO + off);
-        }
-        *reinterpret_cast<u32x4 *>(sQ + mq * kNatStride + dc * 8) = xq;
-        *reinterpret_cast<u32x4 *>(sD + mq * kNatStride + dc * 8) = xd;
-      }
-      // transposed Q / dO tiles, query slots in kslot16 order
-      {
-        const int dgrp = tid & 31, qgrp = tid >> 5;
-        const int u = qgrp >> 1, sub = qgrp & 1;
-        u32x2 vq[8], vd[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int mq = 16 * u + kslot16(8 * sub + jj);
-          const int rl = mq >> log2G;
-          vq[jj] = u32x2{0, 0};
-          vd[jj] = u32x2{0, 0};
-          if (rl < nr) {
-            const int64_t off =
-                (int64_t(r0 + rl) * a.hq + t.g * G + (mq & (G - 1))) * 128 + 4 * dgrp;
-            vq[jj] = *reinterpret_cast<const u32x2 *>(Q + off);
-            vd[jj] = *reinterpret_cast<const u32x2 *>(DO + off);
-          }
-        }
-        store_t8x4(vq, sQt + (4 * dgrp) * kTrStride + 16 * u + 8 * sub, kTrStride);
-        store_t8x4(vd, sDt + (4 * dgrp) * kTrStride + 16 * u + 8 * sub, kTrStride);
-      }
-      if (tid < kQB) {
-        const int rl = tid >> log2G;
-        if (rl < nr) {
-          const int64_t qh = int64_t(r0 + rl) * a.hq + t.g * G + (tid & (G - 1));
-          sL[tid] = LSE[qh] * kLog2e;
-          sDel[tid] = DEL[qh];
-          sB[tid] = BOUND[r0 + rl];
-        } else {
-          sL[tid] = 0.f;
-          sDel[tid] = 0.f;
-          sB[tid] = -1;
-        }
-      }
-      __syncthreads();
-      if (!wave_active) continue;
-
-      // a block needs no mask when every row sees every key of the tile
+  QBlockRegs R;
+  if (nb > 0) {
+    qblock_load(R, a, t, qblock(t, 0, RB, nb_main), tid);
+    qblock_store(R, sQ[0], sD[0], sL[0], sDel[0], sB[0], tid);
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int b = 0; b < nb; ++b) {
+    const QBlock qb = qblock(t, b, RB, nb_main);
+    const bool more = b + 1 < nb;
+    if (more) qblock_load(R, a, t, qblock(t, b + 1, RB, nb_main), tid);
+    if (wave_active) {
+      const u16 *bq = sQ[cur];
+      const u16 *bd = sD[cur];
+      const int32_t *BOUND = qb.src ? a.bound_branch : a.bound_main;
+      // no mask when every row of the block sees every key of the tile
       const bool need_mask =
-          !(nr == RB && t.nkeys == kKTileKeys && BOUND[r0] >= t.kpos0 + kKTileKeys - 1);
-
+          !(qb.nr == RB && t.nkeys == kKTileKeys && BOUND[qb.r0] >= t.kpos0 + kKTileKeys - 1);
       // S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys
       f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int o0 = qi * kNatStride + ks * 16 + hf * 8;
-        const int o1 = (32 + qi) * kNatStride + ks * 16 + hf * 8;
-        s0 = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sQ + o0)), kreg[ks], s0);
-        s1 = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sQ + o1)), kreg[ks], s1);
-        p0 = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sD + o0)), vreg[ks], p0);
-        p1 = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sD + o1)), vreg[ks], p1);
+        s0 = mfma32(lds_nat(bq, 0, ks * 16, lane), kreg[ks], s0);
+        s1 = mfma32(lds_nat(bq, 32, ks * 16, lane), kreg[ks], s1);
+        p0 = mfma32(lds_nat(bd, 0, ks * 16, lane), vreg[ks], p0);
+        p1 = mfma32(lds_nat(bd, 32, ks * 16, lane), vreg[ks], p1);
       }
       float pr[32], ds[32];
 #pragma unroll
       for (int g4 = 0; g4 < 8; ++g4) {
         // queries 32*(g4/4) + 8*(g4%4) + 4*hf + 0..3 are four consecutive slots
         const int q0 = 32 * (g4 >> 2) + 8 * (g4 & 3) + 4 * hf;
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sL + q0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sDel + q0);
-        const int4 b4 = *reinterpret_cast<const int4 *>(sB + q0);
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sL[cur] + q0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sDel[cur] + q0);
+        const int4 b4 = *reinterpret_cast<const int4 *>(sB[cur] + q0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * g4 + e;
           const float sv = v < 16 ? s0[v] : s1[v - 16];
           const float dpv = v < 16 ? p0[v] : p1[v - 16];
-          float p = fast_exp2(sv * sl2 - l4[e]);
+          float p = fast_exp2(fmaf(sv, c, -l4[e]));
           if (need_mask) {
-            const int bq = e == 0 ? b4.x : e == 1 ? b4.y : e == 2 ? b4.z : b4.w;
-            p = (kvalid && kpos <= bq) ? p : 0.f;
+            const int bq4 = e == 0 ? b4.x : e == 1 ? b4.y : e == 2 ? b4.z : b4.w;
+            p = (kvalid && kpos <= bq4) ? p : 0.f;
           }
           pr[v] = p;
           ds[v] = p * (dpv - d4[e]);
         }
       }
-      bf16x8 pb[4], db[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        u32x4 wp, wd;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          wp[p] = pack_bf2(pr[8 * u + 2 * p], pr[8 * u + 2 * p + 1]);
-          wd[p] = pack_bf2(ds[8 * u + 2 * p], ds[8 * u + 2 * p + 1]);
-        }
-        pb[u] = as_bf16x8(wp);
-        db[u] = as_bf16x8(wd);
-      }
       // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 pb = pack8(pr + 8 * u);
+        const bf16x8 db = pack8(ds + 8 * u);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int o = (32 * dt + qi) * kTrStride + 16 * u + 8 * hf;
-          adv[dt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sDt + o)), pb[u], adv[dt]);
-          adk[dt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sQt + o)), db[u], adk[dt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          adv[dt] = mfma32(lds_tr(bd, 16 * u, 32 * dt, lane), pb, adv[dt]);
+          adk[dt] = mfma32(lds_tr(bq, 16 * u, 32 * dt, lane), db, adk[dt]);
         }
+      }
     }
+    if (more) qblock_store(R, sQ[cur ^ 1], sD[cur ^ 1], sL[cur ^ 1], sDel[cur ^ 1], sB[cur ^ 1], tid);
+    __syncthreads();
+    cur ^= 1;
   }
 
   if (!kvalid) return;
@@ -403,10 +347,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d0 = 32 * dt + 8 * a4 + 4 * hf;
       u32x2 wk, wv;
-      wk.x = pack_bf2(adk[dt][4 * a4 + 0] * sc, adk[dt][4 * a4 + 1] * sc);
-      wk.y = pack_bf2(adk[dt][4 * a4 + 2] * sc, adk[dt][4 * a4 + 3] * sc);
-      wv.x = pack_bf2(adv[dt][4 * a4 + 0], adv[dt][4 * a4 + 1]);
-      wv.y = pack_bf2(adv[dt][4 * a4 + 2], adv[dt][4 * a4 + 3]);
+      wk.x = cvt_pk_bf16(adk[dt][4 * a4 + 0] * sc, adk[dt][4 * a4 + 1] * sc);
+      wk.y = cvt_pk_bf16(adk[dt][4 * a4 + 2] * sc, adk[dt][4 * a4 + 3] * sc);
+      wv.x = cvt_pk_bf16(adv[dt][4 * a4 + 0], adv[dt][4 * a4 + 1]);
+      wv.y = cvt_pk_bf16(adv[dt][4 * a4 + 2], adv[dt][4 * a4 + 3]);
       *reinterpret_cast<u32x2 *>(DK + koff + d0) = wk;
       *reinterpret_cast<u32x2 *>(DV + koff + d0) = wv;
     }
