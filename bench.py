@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--cpu-anchors", type=int, default=12,
                     help="anchors in the CPU-oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-kernel event timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -178,6 +180,12 @@ def main():
         return ba.bwd(plan, T["q"], T["k"], T["v"], T["qb"], T["kb"], T["vb"], o, lse, ob, lseb,
                       T["do"], T["dob"], workspace=ws_b)
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()

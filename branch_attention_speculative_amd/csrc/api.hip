@@ -285,15 +285,19 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
 
     float *delta = static_cast<float *>(a->workspace);
     const size_t del_bytes = (size_t(p->n_local + p->n_branch) * p->hq * 4 + 255) & ~size_t(255);
-    float *dq_local = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + del_bytes);
+    float *lse2 = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + del_bytes);
+    float *dq_local = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + 2 * del_bytes);
 
     ba::BwdPreArgs pa{};
     pa.o = a->o;
     pa.ob = a->ob;
     pa.dout = a->dout;
     pa.doutb = a->doutb;
+    pa.lse = a->lse;
+    pa.lseb = a->lseb;
     pa.bound_main = p->dev.bound_main;
     pa.delta = delta;
+    pa.lse2 = lse2;
     pa.n_local = int32_t(p->n_local);
     pa.n_branch = int32_t(p->n_branch);
     pa.hq = p->hq;
@@ -338,6 +342,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     q.lse = a->lse;
     q.lseb = a->lseb;
     q.delta = delta;
+    q.lse2 = lse2;
     q.dq_local = dq_local;
     q.dq = a->dq;
     q.dqb = a->dqb;
@@ -366,6 +371,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     k.lse = a->lse;
     k.lseb = a->lseb;
     k.delta = delta;
+    k.lse2 = lse2;
     k.dk = a->dk;
     k.dv = a->dv;
     k.ktiles = p->dev.ktiles;

@@ -1,5 +1,6 @@
 // Rank-local branch attention (forward partial + Eq. 2 merge, backward) and
-// the backward preprocess Delta = rowsum(dO * O).
+// the backward preprocess Delta = rowsum(dO * O) (with LSE * log2(e) for the
+// ring replay).
 //
 // The branch part is small and stays on the rank that owns the anchor, with
 // no communication (ai.info summary, Key Contributions 1 and Methodology).
@@ -186,11 +187,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
   const int64_t total = (int64_t(a.n_local) + a.n_branch) * a.hq;
   float acc = 0.f;
   bool pad = true;
+  float l2 = 0.f;
   if (pair < total) {
     const int64_t row = pair / a.hq;
     const bool main = row < a.n_local;
     pad = main && a.bound_main[row] < 0;
     const int64_t qh = main ? pair : pair - int64_t(a.n_local) * a.hq;
+    l2 = (main ? a.lse : a.lseb)[qh] * kLog2e;
     const T *O = static_cast<const T *>(main ? a.o : a.ob);
     const T *DO = static_cast<const T *>(main ? a.dout : a.doutb);
     constexpr int PER = DIM / 16;
@@ -204,7 +207,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
-  if (pair < total && sub == 0) a.delta[pair] = pad ? 0.f : acc;
+  if (pair < total && sub == 0) {
+    a.delta[pair] = pad ? 0.f : acc;
+    a.lse2[pair] = pad ? 0.f : l2;
+  }
 }
 
 // ---------------------------------------------------------------------------

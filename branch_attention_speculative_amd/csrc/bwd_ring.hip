@@ -13,9 +13,11 @@
 // rows whose causal bound reaches a key form a suffix).
 //
 // Both kernels keep their streamed tiles (K/V, resp. Q/dO) double-buffered
-// in LDS in row-major form, load the next tile into registers while the
-// current one is computed, and read the operands that are contracted over
-// rows (K^T for dQ; Q^T and dO^T for dK/dV) with the LDS transpose read.
+// in LDS in row-major form, load the next tile straight from global memory
+// into the idle buffer while the current one is computed, and read the
+// operands that are contracted over rows (K^T for dQ; Q^T and dO^T for
+// dK/dV) with the LDS transpose read. P is recomputed from LSE * log2(e),
+// which the backward preprocess stores next to Delta.
 
 #include "kernels.h"
 #include "ring_common.h"
@@ -29,9 +31,47 @@ constexpr int kBN = 64;  // keys per block in the dQ kernel
 // ---------------------------------------------------------------------------
 // dQ: query-stationary ring replay
 
+// One 64-key block, one 32-key tile at a time: S^T = K Q^T, dP^T = V dO^T,
+// dS = P (dP - Delta), dQ^T += K^T dS^T.
+__device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[8],
+                                         const bf16x8 (&dreg)[8], const u16 *bk, const u16 *bv,
+                                         const Seg &cs, int cj0, int bound, float lse2, float delta,
+                                         float c, int lane, int hf) {
+  const bool need_mask = cj0 + kBN > cs.n_full;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x16 s = f32x16{}, p = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s = mfma32(lds_nat(bk, 32 * kt, ks * 16, lane), qreg[ks], s);
+      p = mfma32(lds_nat(bv, 32 * kt, ks * 16, lane), dreg[ks], p);
+    }
+    float ds[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float pv = fast_exp2(fmaf(s[v], c, -lse2));
+      if (need_mask) {
+        const int jj = cj0 + 32 * kt + 8 * (v >> 2) + 4 * hf + (v & 3);
+        const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
+        pv = vis ? pv : 0.f;
+      }
+      ds[v] = pv * (p[v] - delta);
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const bf16x8 db = pack8(ds + 8 * w);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        acc[dt] = mfma32(lds_tr(bk, 32 * kt + 16 * w, 32 * dt, lane), db, acc[dt]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sK[2][kBN * kRS];
-  __shared__ __attribute__((aligned(16))) u16 sV[2][kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sK0[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sV0[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sK1[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sV1[kBN * kRS];
 
   const QTile t = a.qtiles[blockIdx.x];
   if (t.nrows == 0) return;
@@ -49,9 +89,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
   const u16 *V = static_cast<const u16 *>(a.v);
   const int bound = valid ? (t.src ? a.bound_branch[row] : a.bound_main[row]) : -1;
   const int64_t qh = int64_t(row) * a.hq + h;
-  const float lse = valid ? (t.src ? a.lseb[qh] : a.lse[qh]) : 0.f;
-  const float lse2 = (bound >= 0) ? lse * kLog2e : 0.f;
-  const float delta = (bound >= 0) ? a.delta[(t.src ? int64_t(a.n_local) * a.hq : 0) + qh] : 0.f;
+  const int64_t qall = (t.src ? int64_t(a.n_local) * a.hq : 0) + qh;
+  const float lse2 = (bound >= 0) ? a.lse2[qall] : 0.f;
+  const float delta = (bound >= 0) ? a.delta[qall] : 0.f;
 
   bf16x8 qreg[8], dreg[8];
   {
@@ -67,69 +107,44 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
   const float c = a.scale_log2;
+  const int64_t rs = int64_t(a.hkv) * 128;
+  const int g = t.g;
+
+  auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
+    const u16 *kb = K + s.krow * rs + g * 128;
+    const u16 *vb = V + s.krow * rs + g * 128;
+    const int hi = s.n_hi - 1;
+    dma_tile64(dk, [&](int r) { return kb + min(j0 + r, hi) * rs; }, wave, lane);
+    dma_tile64(dv, [&](int r) { return vb + min(j0 + r, hi) * rs; }, wave, lane);
+  };
 
   int sg, j0;
   Seg s;
   first_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
   const int nseg = 2 * a.C;
-  u32x4 RK[4], RV[4];
-  if (sg < nseg) {
-    load_rows64(RK, K, s, j0, t.g, a.hkv, tid);
-    load_rows64(RV, V, s, j0, t.g, a.hkv, tid);
-    store_rows64(RK, sK[0], tid);
-    store_rows64(RV, sV[0], tid);
-  }
+  if (sg < nseg) dma_kv(s, j0, sK0, sV0);
+  dma_wait();
   __syncthreads();
-  int cur = 0;
   while (sg < nseg) {
-    const Seg cs = s;
-    const int cj0 = j0;
-    next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
-    const bool more = sg < nseg;
-    if (more) {
-      load_rows64(RK, K, s, j0, t.g, a.hkv, tid);
-      load_rows64(RV, V, s, j0, t.g, a.hkv, tid);
+    {
+      const Seg cs = s;
+      const int cj0 = j0;
+      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+      if (sg < nseg) dma_kv(s, j0, sK1, sV1);
+      if (wave_active) dq_block(acc, qreg, dreg, sK0, sV0, cs, cj0, bound, lse2, delta, c, lane, hf);
+      dma_wait();
+      __syncthreads();
     }
-    if (wave_active) {
-      const u16 *bk = sK[cur];
-      const u16 *bv = sV[cur];
-      // S^T = K Q^T and dP^T = V dO^T for 64 keys
-      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s0 = mfma32(lds_nat(bk, 0, ks * 16, lane), qreg[ks], s0);
-        s1 = mfma32(lds_nat(bk, 32, ks * 16, lane), qreg[ks], s1);
-        p0 = mfma32(lds_nat(bv, 0, ks * 16, lane), dreg[ks], p0);
-        p1 = mfma32(lds_nat(bv, 32, ks * 16, lane), dreg[ks], p1);
-      }
-      const bool need_mask = cj0 + kBN > cs.n_full;
-      float ds[32];
-#pragma unroll
-      for (int v = 0; v < 32; ++v) {
-        const float sv = v < 16 ? s0[v] : s1[v - 16];
-        const float dpv = v < 16 ? p0[v] : p1[v - 16];
-        float p = fast_exp2(fmaf(sv, c, -lse2));
-        if (need_mask) {
-          const int jj = cj0 + 32 * (v >> 4) + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
-          const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
-          p = vis ? p : 0.f;
-        }
-        ds[v] = p * (dpv - delta);
-      }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 db = pack8(ds + 8 * u);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma32(lds_tr(bk, 16 * u, 32 * dt, lane), db, acc[dt]);
-      }
+    if (sg >= nseg) break;
+    {
+      const Seg cs = s;
+      const int cj0 = j0;
+      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+      if (sg < nseg) dma_kv(s, j0, sK0, sV0);
+      if (wave_active) dq_block(acc, qreg, dreg, sK1, sV1, cs, cj0, bound, lse2, delta, c, lane, hf);
+      dma_wait();
+      __syncthreads();
     }
-    if (more) {
-      store_rows64(RK, sK[cur ^ 1], tid);
-      store_rows64(RV, sV[cur ^ 1], tid);
-    }
-    __syncthreads();
-    cur ^= 1;
   }
 
   if (!valid) return;
@@ -161,15 +176,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
 
 constexpr int kQB = 64;  // query vectors per inner block
 
-struct QBlockRegs {
-  u32x4 q[4], d[4];
-  float l, del;
-  int b;
-};
-
 // Inner blocks are numbered over the main-row range then the branch-row range.
 struct QBlock {
-  int src, r0, nr;
+  int src, r0, nr, hi;
 };
 
 __device__ __forceinline__ QBlock qblock(const KTile &t, int b, int RB, int nb_main) {
@@ -177,69 +186,74 @@ __device__ __forceinline__ QBlock qblock(const KTile &t, int b, int RB, int nb_m
   if (b < nb_main) {
     q.src = 0;
     q.r0 = t.qm_start + b * RB;
-    q.nr = min(RB, t.qm_end - q.r0);
+    q.hi = t.qm_end;
   } else {
     q.src = 1;
     q.r0 = t.qb_start + (b - nb_main) * RB;
-    q.nr = min(RB, t.qb_end - q.r0);
+    q.hi = t.qb_end;
   }
+  q.nr = min(RB, q.hi - q.r0);
   return q;
 }
 
-__device__ __forceinline__ void qblock_load(QBlockRegs &R, const BwdDkdvArgs &a, const KTile &t,
-                                            const QBlock &qb, int tid) {
-  const u16 *Q = static_cast<const u16 *>(qb.src ? a.qb : a.q);
-  const u16 *DO = static_cast<const u16 *>(qb.src ? a.doutb : a.dout);
-  const int G = a.G, log2G = a.log2G;
+// One block of 64 query vectors against this wave's 32 keys, one 32-query
+// tile at a time: S = Q K^T, dP = dO V^T, P, dS, dV^T += dO^T P,
+// dK^T += Q^T dS.
+__device__ __forceinline__ void dkdv_block(f32x16 (&adk)[4], f32x16 (&adv)[4],
+                                           const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
+                                           const u16 *bq, const u16 *bd, const float *sl,
+                                           const float *sdel, const int *sb, bool need_mask,
+                                           int nvalid, bool kvalid, int kpos, float c, int lane,
+                                           int hf) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + 256 * i;
-    const int mq = id >> 4, dc = id & 15;
-    const int rl = mq >> log2G;
-    R.q[i] = u32x4{0, 0, 0, 0};
-    R.d[i] = u32x4{0, 0, 0, 0};
-    if (rl < qb.nr) {
-      const int64_t off = (int64_t(qb.r0 + rl) * a.hq + t.g * G + (mq & (G - 1))) * 128 + dc * 8;
-      R.q[i] = *reinterpret_cast<const u32x4 *>(Q + off);
-      R.d[i] = *reinterpret_cast<const u32x4 *>(DO + off);
-    }
-  }
-  if (tid < kQB) {
-    const int rl = tid >> log2G;
-    R.l = 0.f;
-    R.del = 0.f;
-    R.b = -1;
-    if (rl < qb.nr) {
-      const int64_t qh = int64_t(qb.r0 + rl) * a.hq + t.g * G + (tid & (G - 1));
-      R.l = (qb.src ? a.lseb : a.lse)[qh] * kLog2e;
-      R.del = a.delta[(qb.src ? int64_t(a.n_local) * a.hq : 0) + qh];
-      R.b = (qb.src ? a.bound_branch : a.bound_main)[qb.r0 + rl];
-    }
-  }
-}
-
-__device__ __forceinline__ void qblock_store(const QBlockRegs &R, u16 *sQ, u16 *sD, float *sL,
-                                             float *sDel, int *sB, int tid) {
+  for (int mt = 0; mt < 2; ++mt) {
+    f32x16 s = f32x16{}, p = f32x16{};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + 256 * i;
-    const int mq = id >> 4, dc = id & 15;
-    *reinterpret_cast<u32x4 *>(sQ + mq * kRS + dc * 8) = R.q[i];
-    *reinterpret_cast<u32x4 *>(sD + mq * kRS + dc * 8) = R.d[i];
-  }
-  if (tid < kQB) {
-    sL[tid] = R.l;
-    sDel[tid] = R.del;
-    sB[tid] = R.b;
+    for (int ks = 0; ks < 8; ++ks) {
+      s = mfma32(lds_nat(bq, 32 * mt, ks * 16, lane), kreg[ks], s);
+      p = mfma32(lds_nat(bd, 32 * mt, ks * 16, lane), vreg[ks], p);
+    }
+    float pr[16], ds[16];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // queries 32 mt + 8 g4 + 4 hf + 0..3 are four consecutive slots
+      const int q0 = 32 * mt + 8 * g4 + 4 * hf;
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + q0);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sdel + q0);
+      const int4 b4 = *reinterpret_cast<const int4 *>(sb + q0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * g4 + e;
+        float pv = fast_exp2(fmaf(s[v], c, -l4[e]));
+        if (need_mask) {
+          const int bq4 = e == 0 ? b4.x : e == 1 ? b4.y : e == 2 ? b4.z : b4.w;
+          pv = (kvalid && q0 + e < nvalid && kpos <= bq4) ? pv : 0.f;
+        }
+        pr[v] = pv;
+        ds[v] = pv * (p[v] - d4[e]);
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int u = 2 * mt + w;
+      const bf16x8 pb = pack8(pr + 8 * w);
+      const bf16x8 db = pack8(ds + 8 * w);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        adv[dt] = mfma32(lds_tr(bd, 16 * u, 32 * dt, lane), pb, adv[dt]);
+        adk[dt] = mfma32(lds_tr(bq, 16 * u, 32 * dt, lane), db, adk[dt]);
+      }
+    }
   }
 }
 
 __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sQ[2][kQB * kRS];
-  __shared__ __attribute__((aligned(16))) u16 sD[2][kQB * kRS];
-  __shared__ __attribute__((aligned(16))) float sL[2][kQB];
-  __shared__ __attribute__((aligned(16))) float sDel[2][kQB];
-  __shared__ __attribute__((aligned(16))) int sB[2][kQB];
+  __shared__ __attribute__((aligned(16))) u16 sQ0[kQB * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sD0[kQB * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sQ1[kQB * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sD1[kQB * kRS];
+  __shared__ __attribute__((aligned(16))) float sL0[kQB], sE0[kQB], sL1[kQB], sE1[kQB];
+  __shared__ __attribute__((aligned(16))) int sB0[kQB], sB1[kQB];
 
   const KTile t = a.ktiles[blockIdx.x];
   if (t.nkeys == 0) return;
@@ -252,6 +266,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   const int64_t koff = (krow * a.hkv + t.g) * 128;
   const u16 *K = static_cast<const u16 *>(a.k);
   const u16 *V = static_cast<const u16 *>(a.v);
+  const int G = a.G, log2G = a.log2G;
 
   bf16x8 kreg[8], vreg[8];
 #pragma unroll
@@ -266,75 +281,54 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     adv[dt] = f32x16{};
   }
   const float c = a.scale_log2;
-  const int RB = kQB >> a.log2G;  // rows per inner block
+  const int RB = kQB >> log2G;  // rows per inner block
   const bool wave_active = (wave * 32) < t.nkeys;
   const int nb_main = (t.qm_end - t.qm_start + RB - 1) / RB;
   const int nb = nb_main + (t.qb_end - t.qb_start + RB - 1) / RB;
+  const int hq = a.hq;
 
-  QBlockRegs R;
-  if (nb > 0) {
-    qblock_load(R, a, t, qblock(t, 0, RB, nb_main), tid);
-    qblock_store(R, sQ[0], sD[0], sL[0], sDel[0], sB[0], tid);
-  }
-  __syncthreads();
-  int cur = 0;
-  for (int b = 0; b < nb; ++b) {
+  // issue the loads of inner block b into one buffer set
+  auto dma_block = [&](int b, u16 *dq, u16 *dd, float *dl, float *de, int *db) {
     const QBlock qb = qblock(t, b, RB, nb_main);
-    const bool more = b + 1 < nb;
-    if (more) qblock_load(R, a, t, qblock(t, b + 1, RB, nb_main), tid);
-    if (wave_active) {
-      const u16 *bq = sQ[cur];
-      const u16 *bd = sD[cur];
-      const int32_t *BOUND = qb.src ? a.bound_branch : a.bound_main;
-      // no mask when every row of the block sees every key of the tile
-      const bool need_mask =
-          !(qb.nr == RB && t.nkeys == kKTileKeys && BOUND[qb.r0] >= t.kpos0 + kKTileKeys - 1);
-      // S = Q K^T and dP = dO V^T: 64 queries x this wave's 32 keys
-      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s0 = mfma32(lds_nat(bq, 0, ks * 16, lane), kreg[ks], s0);
-        s1 = mfma32(lds_nat(bq, 32, ks * 16, lane), kreg[ks], s1);
-        p0 = mfma32(lds_nat(bd, 0, ks * 16, lane), vreg[ks], p0);
-        p1 = mfma32(lds_nat(bd, 32, ks * 16, lane), vreg[ks], p1);
-      }
-      float pr[32], ds[32];
-#pragma unroll
-      for (int g4 = 0; g4 < 8; ++g4) {
-        // queries 32*(g4/4) + 8*(g4%4) + 4*hf + 0..3 are four consecutive slots
-        const int q0 = 32 * (g4 >> 2) + 8 * (g4 & 3) + 4 * hf;
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sL[cur] + q0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sDel[cur] + q0);
-        const int4 b4 = *reinterpret_cast<const int4 *>(sB[cur] + q0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * g4 + e;
-          const float sv = v < 16 ? s0[v] : s1[v - 16];
-          const float dpv = v < 16 ? p0[v] : p1[v - 16];
-          float p = fast_exp2(fmaf(sv, c, -l4[e]));
-          if (need_mask) {
-            const int bq4 = e == 0 ? b4.x : e == 1 ? b4.y : e == 2 ? b4.z : b4.w;
-            p = (kvalid && kpos <= bq4) ? p : 0.f;
-          }
-          pr[v] = p;
-          ds[v] = p * (dpv - d4[e]);
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 pb = pack8(pr + 8 * u);
-        const bf16x8 db = pack8(ds + 8 * u);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          adv[dt] = mfma32(lds_tr(bd, 16 * u, 32 * dt, lane), pb, adv[dt]);
-          adk[dt] = mfma32(lds_tr(bq, 16 * u, 32 * dt, lane), db, adk[dt]);
-        }
-      }
-    }
-    if (more) qblock_store(R, sQ[cur ^ 1], sD[cur ^ 1], sL[cur ^ 1], sDel[cur ^ 1], sB[cur ^ 1], tid);
+    const u16 *Q = static_cast<const u16 *>(qb.src ? a.qb : a.q);
+    const u16 *DO = static_cast<const u16 *>(qb.src ? a.doutb : a.dout);
+    const int hb = t.g * G;
+    auto qrow = [&](int mq) {
+      return (int64_t(min(qb.r0 + (mq >> log2G), qb.hi - 1)) * hq + hb + (mq & (G - 1))) * 128;
+    };
+    dma_tile64(dq, [&](int mq) { return Q + qrow(mq); }, wave, lane);
+    dma_tile64(dd, [&](int mq) { return DO + qrow(mq); }, wave, lane);
+    const int64_t base = qb.src ? int64_t(a.n_local) * hq : 0;
+    const int rr = min(qb.r0 + (lane >> log2G), qb.hi - 1);
+    const int64_t qh = base + int64_t(rr) * hq + hb + (lane & (G - 1));
+    if (wave == 1) dma_dword64(dl, a.lse2 + qh);
+    if (wave == 2) dma_dword64(de, a.delta + qh);
+    if (wave == 3) dma_dword64(db, (qb.src ? a.bound_branch : a.bound_main) + rr);
+  };
+  auto compute = [&](int b, const u16 *bq, const u16 *bd, const float *sl, const float *se,
+                     const int *sb) {
+    const QBlock qb = qblock(t, b, RB, nb_main);
+    const int32_t *BOUND = qb.src ? a.bound_branch : a.bound_main;
+    // no mask when every row of the block sees every key of the tile
+    const bool need_mask =
+        !(qb.nr == RB && t.nkeys == kKTileKeys && BOUND[qb.r0] >= t.kpos0 + kKTileKeys - 1);
+    dkdv_block(adk, adv, kreg, vreg, bq, bd, sl, se, sb, need_mask, qb.nr << log2G, kvalid, kpos,
+               c, lane, hf);
+  };
+
+  if (nb > 0) dma_block(0, sQ0, sD0, sL0, sE0, sB0);
+  dma_wait();
+  __syncthreads();
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) dma_block(b + 1, sQ1, sD1, sL1, sE1, sB1);
+    if (wave_active) compute(b, sQ0, sD0, sL0, sE0, sB0);
+    dma_wait();
     __syncthreads();
-    cur ^= 1;
+    if (b + 1 >= nb) break;
+    if (b + 2 < nb) dma_block(b + 2, sQ0, sD0, sL0, sE0, sB0);
+    if (wave_active) compute(b + 1, sQ1, sD1, sL1, sE1, sB1);
+    dma_wait();
+    __syncthreads();
   }
 
   if (!kvalid) return;

@@ -19,8 +19,8 @@
 // transpose read, in the key order the score registers come in.
 //
 // Pipelining: K/V tiles are double-buffered in LDS and the next block is
-// loaded into registers while the current one is computed (one barrier per
-// block). The running max is only raised when a block's max exceeds it by
+// loaded straight from global memory into the idle buffer while the current
+// one is computed (one barrier per block). The running max is only raised when a block's max exceeds it by
 // more than 2^8 (in exp2 units), so most blocks skip the O rescale; the
 // exponentials stay below 2^8 and the final normalisation uses the same max.
 
@@ -34,9 +34,74 @@ namespace {
 constexpr int kBN = 64;          // keys per block
 constexpr float kLazyMax = 8.f;  // rescale threshold (log2 units)
 
+struct FwdState {
+  bf16x8 qreg[8];
+  f32x16 acc[4];
+  float mrun, lsum;
+};
+
+// One 64-key block: scores, online softmax update, O += P V.
+__device__ __forceinline__ void fwd_block(FwdState &st, const u16 *bk, const u16 *bv, const Seg &cs,
+                                          int cj0, int bound, float c, int lane, int hf) {
+  // S^T = K Q^T for 64 keys (two 32-key tiles)
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    s0 = mfma32(lds_nat(bk, 0, ks * 16, lane), st.qreg[ks], s0);
+    s1 = mfma32(lds_nat(bk, 32, ks * 16, lane), st.qreg[ks], s1);
+  }
+  float x[32];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    x[v] = s0[v];
+    x[16 + v] = s1[v];
+  }
+  if (cj0 + kBN > cs.n_full) {
+#pragma unroll
+    for (int v = 0; v < 32; ++v) {
+      const int jj = cj0 + 32 * (v >> 4) + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
+      const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
+      x[v] = vis ? x[v] : kNegInf;
+    }
+  }
+  float bmax = x[0];
+#pragma unroll
+  for (int v = 1; v < 32; ++v) bmax = fmaxf(bmax, x[v]);
+  bmax = fmaxf(bmax, wave_shfl_xor32(bmax));
+  const float cand = bmax * c;
+  const bool up = cand > st.mrun + kLazyMax;
+  if (__any(up)) {
+    const float mnew = up ? cand : st.mrun;
+    const float alpha = (mnew == st.mrun) ? 1.f : fast_exp2(st.mrun - mnew);
+    st.mrun = mnew;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.acc[dt] *= alpha;
+  }
+  const float mu = (st.mrun == kNegInf) ? 0.f : st.mrun;
+  float psum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 32; ++v) {
+    x[v] = fast_exp2(fmaf(x[v], c, -mu));
+    psum += x[v];
+  }
+  st.lsum += psum;
+  // O^T += V^T P^T
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const bf16x8 pb = pack8(x + 8 * u);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.acc[dt] = mfma32(lds_tr(bv, 16 * u, 32 * dt, lane), pb, st.acc[dt]);
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sK[2][kBN * kRS];
-  __shared__ __attribute__((aligned(16))) u16 sV[2][kBN * kRS];
+  // double-buffered K/V tiles; separate objects so the LDS loads into one
+  // buffer never order the reads of the other
+  __shared__ __attribute__((aligned(16))) u16 sK0[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sV0[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sK1[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sV1[kBN * kRS];
 
   const QTile t = a.qtiles[blockIdx.x];
   if (t.nrows == 0) return;
@@ -53,111 +118,64 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
   const u16 *V = static_cast<const u16 *>(a.v);
   const int bound = valid ? (t.src ? a.bound_branch[row] : a.bound_main[row]) : -1;
 
-  bf16x8 qreg[8];
+  FwdState st;
   {
     const u16 *qp = Q + (int64_t(row) * a.hq + h) * 128 + hf * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       u32x4 x = valid ? *reinterpret_cast<const u32x4 *>(qp + ks * 16) : u32x4{0, 0, 0, 0};
-      qreg[ks] = as_bf16x8(x);
+      st.qreg[ks] = as_bf16x8(x);
     }
   }
-
-  f32x16 acc[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  float mrun = kNegInf, lsum = 0.f;
+  for (int dt = 0; dt < 4; ++dt) st.acc[dt] = f32x16{};
+  st.mrun = kNegInf;
+  st.lsum = 0.f;
   const float c = a.scale_log2;
+  const int64_t rs = int64_t(a.hkv) * 128;
+  const int g = t.g;
+
+  auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
+    const u16 *kb = K + s.krow * rs + g * 128;
+    const u16 *vb = V + s.krow * rs + g * 128;
+    const int last = s.n_hi - 1 - j0;
+    dma_tile64(dk, [&](int r) { return kb + min(j0 + r, j0 + last) * rs; }, wave, lane);
+    dma_tile64(dv, [&](int r) { return vb + min(j0 + r, j0 + last) * rs; }, wave, lane);
+  };
 
   int sg, j0;
   Seg s;
   first_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
   const int nseg = 2 * a.C;
-  u32x4 RK[4], RV[4];
-  if (sg < nseg) {
-    load_rows64(RK, K, s, j0, t.g, a.hkv, tid);
-    load_rows64(RV, V, s, j0, t.g, a.hkv, tid);
-    store_rows64(RK, sK[0], tid);
-    store_rows64(RV, sV[0], tid);
-  }
+  if (sg < nseg) dma_kv(s, j0, sK0, sV0);
+  dma_wait();
   __syncthreads();
-  int cur = 0;
   while (sg < nseg) {
-    const Seg cs = s;
-    const int cj0 = j0;
-    next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
-    const bool more = sg < nseg;
-    if (more) {  // in flight while this block is computed
-      load_rows64(RK, K, s, j0, t.g, a.hkv, tid);
-      load_rows64(RV, V, s, j0, t.g, a.hkv, tid);
+    {
+      const Seg cs = s;
+      const int cj0 = j0;
+      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+      if (sg < nseg) dma_kv(s, j0, sK1, sV1);
+      if (wave_active) fwd_block(st, sK0, sV0, cs, cj0, bound, c, lane, hf);
+      dma_wait();
+      __syncthreads();
     }
-    if (wave_active) {
-      const u16 *bk = sK[cur];
-      const u16 *bv = sV[cur];
-      // S^T = K Q^T for 64 keys (two 32-key tiles)
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s0 = mfma32(lds_nat(bk, 0, ks * 16, lane), qreg[ks], s0);
-        s1 = mfma32(lds_nat(bk, 32, ks * 16, lane), qreg[ks], s1);
-      }
-      float x[32];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        x[v] = s0[v];
-        x[16 + v] = s1[v];
-      }
-      if (cj0 + kBN > cs.n_full) {
-#pragma unroll
-        for (int v = 0; v < 32; ++v) {
-          const int jj = cj0 + 32 * (v >> 4) + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
-          const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
-          x[v] = vis ? x[v] : kNegInf;
-        }
-      }
-      float bmax = x[0];
-#pragma unroll
-      for (int v = 1; v < 32; ++v) bmax = fmaxf(bmax, x[v]);
-      bmax = fmaxf(bmax, wave_shfl_xor32(bmax));
-      const float cand = bmax * c;
-      const bool up = cand > mrun + kLazyMax;
-      if (__any(up)) {
-        const float mnew = up ? cand : mrun;
-        const float alpha = (mnew == mrun) ? 1.f : fast_exp2(mrun - mnew);
-        mrun = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
-      }
-      const float mu = (mrun == kNegInf) ? 0.f : mrun;
-      float psum = 0.f;
-#pragma unroll
-      for (int v = 0; v < 32; ++v) {
-        x[v] = fast_exp2(fmaf(x[v], c, -mu));
-        psum += x[v];
-      }
-      lsum += psum;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pb[u] = pack8(x + 8 * u);
-      // O^T += V^T P^T
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma32(lds_tr(bv, 16 * u, 32 * dt, lane), pb[u], acc[dt]);
+    if (sg >= nseg) break;
+    {
+      const Seg cs = s;
+      const int cj0 = j0;
+      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+      if (sg < nseg) dma_kv(s, j0, sK0, sV0);
+      if (wave_active) fwd_block(st, sK1, sV1, cs, cj0, bound, c, lane, hf);
+      dma_wait();
+      __syncthreads();
     }
-    if (more) {
-      store_rows64(RK, sK[cur ^ 1], tid);
-      store_rows64(RV, sV[cur ^ 1], tid);
-    }
-    __syncthreads();
-    cur ^= 1;
   }
 
   if (!valid) return;
-  const float ltot = lsum + wave_shfl_xor32(lsum);
+  const float ltot = st.lsum + wave_shfl_xor32(st.lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  const float lse = ltot > 0.f ? (mrun + log2f(ltot)) * kLn2 : kNegInf;
+  const float lse = ltot > 0.f ? (st.mrun + log2f(ltot)) * kLn2 : kNegInf;
   const int64_t ob = (int64_t(row) * a.hq + h) * 128;
   if (t.src == 0) {
     u16 *O = static_cast<u16 *>(a.o);
@@ -167,8 +185,8 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = 32 * dt + 8 * a4 + 4 * hf;
         u32x2 w;
-        w.x = cvt_pk_bf16(acc[dt][4 * a4 + 0] * inv, acc[dt][4 * a4 + 1] * inv);
-        w.y = cvt_pk_bf16(acc[dt][4 * a4 + 2] * inv, acc[dt][4 * a4 + 3] * inv);
+        w.x = cvt_pk_bf16(st.acc[dt][4 * a4 + 0] * inv, st.acc[dt][4 * a4 + 1] * inv);
+        w.y = cvt_pk_bf16(st.acc[dt][4 * a4 + 2] * inv, st.acc[dt][4 * a4 + 3] * inv);
         *reinterpret_cast<u32x2 *>(O + ob + d0) = w;
       }
     if (hf == 0) a.lse[int64_t(row) * a.hq + h] = lse;
@@ -178,8 +196,8 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = 32 * dt + 8 * a4 + 4 * hf;
-        f32x4 w = {acc[dt][4 * a4 + 0] * inv, acc[dt][4 * a4 + 1] * inv,
-                   acc[dt][4 * a4 + 2] * inv, acc[dt][4 * a4 + 3] * inv};
+        f32x4 w = {st.acc[dt][4 * a4 + 0] * inv, st.acc[dt][4 * a4 + 1] * inv,
+                   st.acc[dt][4 * a4 + 2] * inv, st.acc[dt][4 * a4 + 3] * inv};
         *reinterpret_cast<f32x4 *>(a.om + ob + d0) = w;
       }
     if (hf == 0) a.lm[int64_t(row) * a.hq + h] = lse;

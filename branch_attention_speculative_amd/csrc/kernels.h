@@ -40,8 +40,10 @@ struct FwdBranchArgs {
 // Delta = rowsum(dO * O) for main rows then branch rows.
 struct BwdPreArgs {
   const void *o, *ob, *dout, *doutb;
+  const float *lse, *lseb;
   const int32_t *bound_main;
   float *delta;  // [(N + NB) * hq]
+  float *lse2;   // [(N + NB) * hq]: LSE * log2(e)
   int32_t n_local, n_branch, hq, d;
 };
 
@@ -61,6 +63,7 @@ struct BwdBranchArgs {
 struct BwdDqArgs {
   const void *q, *qb, *k, *v, *dout, *doutb;
   const float *lse, *lseb, *delta;  // delta: main rows then branch rows
+  const float *lse2;                // LSE * log2(e), main rows then branch rows
   const float *dq_local;            // branch rows: branch-key share of dQ
   void *dq, *dqb;
   const QTile *qtiles;
@@ -72,7 +75,7 @@ struct BwdDqArgs {
 // Ring replay for dK/dV (key-stationary).
 struct BwdDkdvArgs {
   const void *q, *qb, *k, *v, *dout, *doutb;
-  const float *lse, *lseb, *delta;
+  const float *lse, *lseb, *delta, *lse2;
   void *dk, *dv;
   const KTile *ktiles;
   const int32_t *bound_main, *bound_branch;

@@ -39,10 +39,10 @@ size_t ws_fwd_bytes(const ba_plan &p) {
   return align256(size_t(p.n_branch) * p.hq * p.d * 4) + align256(size_t(p.n_branch) * p.hq * 4);
 }
 
-// Backward workspace: Delta of every row (main then branch, fp32) and the
-// branch-local share of dQ of every branch row (fp32).
+// Backward workspace: Delta and LSE * log2(e) of every row (main then
+// branch, fp32) and the branch-local share of dQ of every branch row (fp32).
 size_t ws_bwd_bytes(const ba_plan &p) {
-  return align256(size_t(p.n_local + p.n_branch) * p.hq * 4) +
+  return 2 * align256(size_t(p.n_local + p.n_branch) * p.hq * 4) +
          align256(size_t(p.n_branch) * p.hq * p.d * 4);
 }
 

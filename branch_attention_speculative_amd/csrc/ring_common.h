@@ -1,5 +1,6 @@
 // Pieces shared by the bf16 matrix-core ring kernels: the ring walk over
-// (step, chunk) segments and the LDS operand reads.
+// (step, chunk) segments, the swizzled LDS tile layout with its operand reads,
+// and the direct global -> LDS tile loads.
 #pragma once
 
 #include "common.h"
@@ -9,8 +10,8 @@ namespace ba {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kRS = 136;  // LDS row stride (bf16) of natural [row][128] tiles
+typedef __attribute__((address_space(1))) const void *gptr_t;
+typedef __attribute__((address_space(3))) void *lptr_t;
 
 // Two floats -> packed bf16x2 with the hardware round-to-nearest-even convert.
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
@@ -26,32 +27,77 @@ __device__ __forceinline__ bf16x8 pack8(const float *x) {
   return as_bf16x8(w);
 }
 
-// Natural operand from a row-major LDS tile X[row][col] (row stride kRS):
-// lane l takes row row0 + l%32 and the 8 columns col0 + 8*(l/32) .. +7.
-// Serves A operands (rows = M, cols = K) and B operands (rows = N, cols = K).
-__device__ __forceinline__ bf16x8 lds_nat(const u16 *X, int row0, int col0, int lane) {
-  return as_bf16x8(
-      *reinterpret_cast<const u32x4 *>(X + (row0 + (lane & 31)) * kRS + col0 + 8 * (lane >> 5)));
+// ---- LDS tile layout ------------------------------------------------------
+// Tiles hold 64 rows x 128 bf16 columns, row-major with 256-byte rows (no
+// padding). Bank conflicts are avoided by an XOR swizzle of the 16-byte
+// chunks: logical chunk c of row r sits at physical chunk c ^ swz(r), with
+// swz(r) = ((r & 3) << 2) | ((r >> 2) & 3). Measured on gfx950 with the
+// SQ_LDS_BANK_CONFLICT counter, both access patterns below are conflict-free
+// under it: 16 lanes reading one 16-byte chunk of 16 consecutive rows, and the
+// transpose read (4 rows x 4 consecutive chunks per pair of 16-lane groups).
+constexpr int kRS = 128;  // LDS row stride (bf16 elements)
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// element offset of (row, col) in a swizzled tile
+__device__ __forceinline__ int toff(int r, int col) {
+  return r * kRS + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
 }
 
-// Transposed operand from a row-major LDS tile X[k][m] (row stride kRS), for
-// a contraction over the tile's rows: the operand element (m, slot s) is
-// X[k0 + kslot16(s)][m0 + m]. Two ds_read_b64_tr_b16 per lane: inside each
-// 16-lane group, lane j receives element j%4 of the 8-byte chunks addressed
-// by lanes 4e + j/4 (e = 0..3), so pointing lane i at row (i/4) and column
-// chunk (i%4) hands lane j four consecutive rows of column j.
+// Natural operand from a tile X[row][col]: lane l takes row row0 + l%32 and
+// the 8 columns col0 + 8*(l/32) .. +7 (col0 a multiple of 16). Serves A
+// operands (rows = M, cols = K) and B operands (rows = N, cols = K).
+__device__ __forceinline__ bf16x8 lds_nat(const u16 *X, int row0, int col0, int lane) {
+  return as_bf16x8(
+      *reinterpret_cast<const u32x4 *>(X + toff(row0 + (lane & 31), col0 + 8 * (lane >> 5))));
+}
+
+// Transposed operand from a tile X[k][m], for a contraction over the tile's
+// rows: the operand element (m, slot s) is X[k0 + kslot16(s)][m0 + m]. Two
+// ds_read_b64_tr_b16 per lane: inside each 16-lane group, lane j receives
+// element j%4 of the 8-byte chunks addressed by lanes 4e + j/4 (e = 0..3), so
+// pointing lane i at row (i/4) and column chunk (i%4) hands lane j four
+// consecutive rows of column j.
 __device__ __forceinline__ bf16x8 lds_tr(const u16 *X, int k0, int m0, int lane) {
   const int g = lane >> 4, i = lane & 15;
   const int mb = (g & 1) << 4, h = g >> 1;
-  const u16 *p0 = X + (k0 + 4 * h + (i >> 2)) * kRS + m0 + mb + 4 * (i & 3);
-  const u16 *p1 = p0 + 8 * kRS;
+  const int r0 = k0 + 4 * h + (i >> 2);
+  const int col = m0 + mb + 4 * (i & 3);
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p1));
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(X + toff(r0, col)));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(X + toff(r0 + 8, col)));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, c);
 }
+
+// Direct global -> LDS load of a 64-row x 128-col bf16 tile into the
+// swizzled layout. global_load_lds_dwordx4 writes lane i's 16 bytes at the
+// wave-uniform LDS base + 16 i, so each wave instruction fills 64 consecutive
+// physical chunks (4 rows); lane i of instruction J fills row 4J + i/16,
+// physical chunk i%16, i.e. logical chunk (i%16) ^ swz(row). The 16
+// instructions of a tile are shared by the 4 waves of the workgroup.
+// rowaddr(row) gives the global address of a row's first element and must
+// stay in bounds. Completion is tracked by vmcnt: dma_wait() before the
+// barrier that publishes the tile.
+template <class RowAddr>
+__device__ __forceinline__ void dma_tile64(u16 *lds_tile, RowAddr rowaddr, int wave, int lane) {
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int J = wave + 4 * jj;
+    const int row = 4 * J + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);
+    const u16 *src = rowaddr(row) + 8 * c;
+    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lds_tile + 512 * J), 16, 0, 0);
+  }
+}
+
+// 64 consecutive 4-byte values (lane i -> element i) into LDS.
+__device__ __forceinline__ void dma_dword64(void *lds_dst, const void *src_lane) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src_lane, (lptr_t)lds_dst, 4, 0, 0);
+}
+
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---- ring walk ------------------------------------------------------------
 
@@ -96,29 +142,6 @@ __device__ __forceinline__ void next_block(int &sg, int &j0, Seg &s, const QTile
   for (++sg; sg < 2 * C; ++sg) {
     s = seg_info(sg, t, C, r, n_local);
     if (s.n_hi > 0) return;
-  }
-}
-
-// Load a 64-row x 128-col bf16 block of K or V rows krow + min(j0 + i, n_hi - 1)
-// into registers: 256 threads x 4 x 16 bytes.
-__device__ __forceinline__ void load_rows64(u32x4 (&R)[4], const u16 *__restrict__ X, const Seg &s,
-                                           int j0, int g, int hkv, int tid) {
-  const int64_t rs = int64_t(hkv) * 128;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + 256 * i;
-    const int row = id >> 4, dc = id & 15;
-    const int kk = min(j0 + row, s.n_hi - 1);
-    R[i] = *reinterpret_cast<const u32x4 *>(X + (s.krow + kk) * rs + g * 128 + dc * 8);
-  }
-}
-
-__device__ __forceinline__ void store_rows64(const u32x4 (&R)[4], u16 *dst, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + 256 * i;
-    const int row = id >> 4, dc = id & 15;
-    *reinterpret_cast<u32x4 *>(dst + row * kRS + dc * 8) = R[i];
   }
 }
 
