@@ -196,96 +196,139 @@ __device__ __forceinline__ QBlock qblock(const KTile &t, int b, int RB, int nb_m
   return q;
 }
 
-// One block of 64 query vectors against this wave's 32 keys, one 32-query
-// tile at a time: S = Q K^T, dP = dO V^T, P, dS, dV^T += dO^T P,
-// dK^T += Q^T dS.
-__device__ __forceinline__ void dkdv_block(f32x16 (&adk)[4], f32x16 (&adv)[4],
-                                           const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
-                                           const u16 *bq, const u16 *bd, const float *sl,
-                                           const float *sdel, const int *sb, bool need_mask,
-                                           int nvalid, bool kvalid, int kpos, float c, int lane,
-                                           int hf) {
+// The eight waves of a dK/dV workgroup come in pairs that own the same 32
+// keys and sit on the same SIMD. The first wave of a pair computes S = Q K^T,
+// P = exp(S - LSE) and dV^T += dO^T P; it also hands P (bf16, in its MFMA
+// register layout) to its partner through LDS. The partner computes
+// dP = dO V^T and, once P is published by a barrier, dS = P (dP - Delta) and
+// dK^T += Q^T dS. Each wave then needs about half the registers of one wave
+// doing all four products, so two waves fit on each SIMD and overlap each
+// other's vector and matrix-core phases, with no duplicated products.
+
+constexpr int kXchg = 4 * 64 * 4;  // u32 per wave pair: 4 bf16x8 operands x 64 lanes
+
+// dV wave, phase 1 of a block: S and P for 64 query vectors; P goes to the
+// exchange slot (xs) and stays in pb for phase 2.
+template <bool MASK>
+__device__ __forceinline__ void dv_phase1(bf16x8 (&pb)[4], const bf16x8 (&kreg)[8], const u16 *bq,
+                                          const float *sl, const int *sb, uint32_t *xs, int nvalid,
+                                          bool kvalid, int kpos, float c, int lane, int hf) {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    f32x16 s = f32x16{}, p = f32x16{};
+    f32x16 s = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      s = mfma32(lds_nat(bq, 32 * mt, ks * 16, lane), kreg[ks], s);
-      p = mfma32(lds_nat(bd, 32 * mt, ks * 16, lane), vreg[ks], p);
-    }
-    float pr[16], ds[16];
+    for (int ks = 0; ks < 8; ++ks) s = mfma32(lds_nat(bq, 32 * mt, ks * 16, lane), kreg[ks], s);
+    float pr[16];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       // queries 32 mt + 8 g4 + 4 hf + 0..3 are four consecutive slots
       const int q0 = 32 * mt + 8 * g4 + 4 * hf;
       const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + q0);
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sdel + q0);
-      const int4 b4 = *reinterpret_cast<const int4 *>(sb + q0);
+      int4 b4 = {0, 0, 0, 0};
+      if (MASK) b4 = *reinterpret_cast<const int4 *>(sb + q0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int v = 4 * g4 + e;
-        float pv = fast_exp2(fmaf(s[v], c, -l4[e]));
-        if (need_mask) {
+        float pv = fast_exp2(fmaf(s[4 * g4 + e], c, -l4[e]));
+        if (MASK) {
           const int bq4 = e == 0 ? b4.x : e == 1 ? b4.y : e == 2 ? b4.z : b4.w;
           pv = (kvalid && q0 + e < nvalid && kpos <= bq4) ? pv : 0.f;
         }
-        pr[v] = pv;
-        ds[v] = pv * (p[v] - d4[e]);
+        pr[4 * g4 + e] = pv;
       }
     }
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       const int u = 2 * mt + w;
-      const bf16x8 pb = pack8(pr + 8 * w);
-      const bf16x8 db = pack8(ds + 8 * w);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        adv[dt] = mfma32(lds_tr(bd, 16 * u, 32 * dt, lane), pb, adv[dt]);
-        adk[dt] = mfma32(lds_tr(bq, 16 * u, 32 * dt, lane), db, adk[dt]);
-      }
+      pb[u] = pack8(pr + 8 * w);
+      *reinterpret_cast<u32x4 *>(xs + (u * 64 + lane) * 4) = __builtin_bit_cast(u32x4, pb[u]);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
+// dV wave, phase 2: dV^T += dO^T P.
+__device__ __forceinline__ void dv_phase2(f32x16 (&adv)[4], const bf16x8 (&pb)[4], const u16 *bd,
+                                          int lane) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) adv[dt] = mfma32(lds_tr(bd, 16 * u, 32 * dt, lane), pb[u], adv[dt]);
+}
+
+// dK wave, phase 1: dP = dO V^T for 64 query vectors.
+__device__ __forceinline__ void dk_phase1(f32x16 (&dp)[2], const bf16x8 (&vreg)[8], const u16 *bd,
+                                          int lane) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    f32x16 p = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) p = mfma32(lds_nat(bd, 32 * mt, ks * 16, lane), vreg[ks], p);
+    dp[mt] = p;
+  }
+}
+
+// dK wave, phase 2: dS = P (dP - Delta) with P from the exchange slot,
+// dK^T += Q^T dS.
+__device__ __forceinline__ void dk_phase2(f32x16 (&adk)[4], const f32x16 (&dp)[2], const u16 *bq,
+                                          const float *sdel, const uint32_t *xs, int lane, int hf) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    float ds[16];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const u32x4 pw = *reinterpret_cast<const u32x4 *>(xs + ((2 * mt + w) * 64 + lane) * 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ds[8 * w + 2 * k] = __uint_as_float(pw[k] << 16);
+        ds[8 * w + 2 * k + 1] = __uint_as_float(pw[k] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int q0 = 32 * mt + 8 * g4 + 4 * hf;
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sdel + q0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * g4 + e;
+        ds[v] = ds[v] * (dp[mt][v] - d4[e]);
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const bf16x8 db = pack8(ds + 8 * w);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        adk[dt] = mfma32(lds_tr(bq, 16 * (2 * mt + w), 32 * dt, lane), db, adk[dt]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sQ0[kQB * kRS];
   __shared__ __attribute__((aligned(16))) u16 sD0[kQB * kRS];
   __shared__ __attribute__((aligned(16))) u16 sQ1[kQB * kRS];
   __shared__ __attribute__((aligned(16))) u16 sD1[kQB * kRS];
   __shared__ __attribute__((aligned(16))) float sL0[kQB], sE0[kQB], sL1[kQB], sE1[kQB];
   __shared__ __attribute__((aligned(16))) int sB0[kQB], sB1[kQB];
+  __shared__ __attribute__((aligned(16))) uint32_t sX[4 * kXchg];
 
   const KTile t = a.ktiles[blockIdx.x];
   if (t.nkeys == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int role = wave >> 2;  // 0: S, P, dV wave; 1: dP, dS, dK wave
   const int qi = lane & 31, hf = lane >> 5;
-  const int kk = wave * 32 + qi;  // this lane's key inside the tile
+  const int kk = (wave & 3) * 32 + qi;  // this lane's key inside the tile
   const bool kvalid = kk < t.nkeys;
   const int kpos = t.kpos0 + kk;
   const int64_t krow = int64_t(t.shard) * a.n_local + t.krow0 + min(kk, t.nkeys - 1);
   const int64_t koff = (krow * a.hkv + t.g) * 128;
-  const u16 *K = static_cast<const u16 *>(a.k);
-  const u16 *V = static_cast<const u16 *>(a.v);
   const int G = a.G, log2G = a.log2G;
-
-  bf16x8 kreg[8], vreg[8];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(K + koff + ks * 16 + hf * 8));
-    vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(V + koff + ks * 16 + hf * 8));
-  }
-  f32x16 adk[4], adv[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    adk[dt] = f32x16{};
-    adv[dt] = f32x16{};
-  }
   const float c = a.scale_log2;
   const int RB = kQB >> log2G;  // rows per inner block
-  const bool wave_active = (wave * 32) < t.nkeys;
+  const bool wave_active = ((wave & 3) * 32) < t.nkeys;
   const int nb_main = (t.qm_end - t.qm_start + RB - 1) / RB;
   const int nb = nb_main + (t.qb_end - t.qb_start + RB - 1) / RB;
   const int hq = a.hq;
+  uint32_t *xs = sX + (wave & 3) * kXchg;
 
   // issue the loads of inner block b into one buffer set
   auto dma_block = [&](int b, u16 *dq, u16 *dd, float *dl, float *de, int *db) {
@@ -296,8 +339,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     auto qrow = [&](int mq) {
       return (int64_t(min(qb.r0 + (mq >> log2G), qb.hi - 1)) * hq + hb + (mq & (G - 1))) * 128;
     };
-    dma_tile64(dq, [&](int mq) { return Q + qrow(mq); }, wave, lane);
-    dma_tile64(dd, [&](int mq) { return DO + qrow(mq); }, wave, lane);
+    dma_tile64<8>(dq, [&](int mq) { return Q + qrow(mq); }, wave, lane);
+    dma_tile64<8>(dd, [&](int mq) { return DO + qrow(mq); }, wave, lane);
     const int64_t base = qb.src ? int64_t(a.n_local) * hq : 0;
     const int rr = min(qb.r0 + (lane >> log2G), qb.hi - 1);
     const int64_t qh = base + int64_t(rr) * hq + hb + (lane & (G - 1));
@@ -305,48 +348,85 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     if (wave == 2) dma_dword64(de, a.delta + qh);
     if (wave == 3) dma_dword64(db, (qb.src ? a.bound_branch : a.bound_main) + rr);
   };
-  auto compute = [&](int b, const u16 *bq, const u16 *bd, const float *sl, const float *se,
-                     const int *sb) {
+  auto need_mask = [&](int b) {
     const QBlock qb = qblock(t, b, RB, nb_main);
     const int32_t *BOUND = qb.src ? a.bound_branch : a.bound_main;
     // no mask when every row of the block sees every key of the tile
-    const bool need_mask =
-        !(qb.nr == RB && t.nkeys == kKTileKeys && BOUND[qb.r0] >= t.kpos0 + kKTileKeys - 1);
-    dkdv_block(adk, adv, kreg, vreg, bq, bd, sl, se, sb, need_mask, qb.nr << log2G, kvalid, kpos,
-               c, lane, hf);
+    return !(qb.nr == RB && t.nkeys == kKTileKeys && BOUND[qb.r0] >= t.kpos0 + kKTileKeys - 1);
   };
+  auto nvalid = [&](int b) { return qblock(t, b, RB, nb_main).nr << log2G; };
 
+  // operand registers: K for the S wave, V for the dP wave
+  const u16 *KV = static_cast<const u16 *>(role ? a.v : a.k);
+  bf16x8 kvreg[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    kvreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(KV + koff + ks * 16 + hf * 8));
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+  // Every block: phase 1, a barrier that publishes P, phase 2, then the
+  // barrier that publishes the next block's tiles. The two roles run their
+  // own loops with the same barrier sequence.
   if (nb > 0) dma_block(0, sQ0, sD0, sL0, sE0, sB0);
   dma_wait();
   __syncthreads();
-  for (int b = 0; b < nb; b += 2) {
-    if (b + 1 < nb) dma_block(b + 1, sQ1, sD1, sL1, sE1, sB1);
-    if (wave_active) compute(b, sQ0, sD0, sL0, sE0, sB0);
-    dma_wait();
-    __syncthreads();
-    if (b + 1 >= nb) break;
-    if (b + 2 < nb) dma_block(b + 2, sQ0, sD0, sL0, sE0, sB0);
-    if (wave_active) compute(b + 1, sQ1, sD1, sL1, sE1, sB1);
-    dma_wait();
-    __syncthreads();
+  if (role == 0) {
+    auto blk = [&](int b, const u16 *bq, const u16 *bd, const float *sl, const int *sb) {
+      bf16x8 pb[4];
+      if (wave_active) {
+        if (need_mask(b))
+          dv_phase1<true>(pb, kvreg, bq, sl, sb, xs, nvalid(b), kvalid, kpos, c, lane, hf);
+        else
+          dv_phase1<false>(pb, kvreg, bq, sl, sb, xs, nvalid(b), kvalid, kpos, c, lane, hf);
+      }
+      __syncthreads();
+      if (wave_active) dv_phase2(acc, pb, bd, lane);
+    };
+    for (int b = 0; b < nb; b += 2) {
+      if (b + 1 < nb) dma_block(b + 1, sQ1, sD1, sL1, sE1, sB1);
+      blk(b, sQ0, sD0, sL0, sB0);
+      dma_wait();
+      __syncthreads();
+      if (b + 1 >= nb) break;
+      if (b + 2 < nb) dma_block(b + 2, sQ0, sD0, sL0, sE0, sB0);
+      blk(b + 1, sQ1, sD1, sL1, sB1);
+      dma_wait();
+      __syncthreads();
+    }
+  } else {
+    auto blk = [&](const u16 *bq, const u16 *bd, const float *se) {
+      f32x16 dp[2];
+      if (wave_active) dk_phase1(dp, kvreg, bd, lane);
+      __syncthreads();
+      if (wave_active) dk_phase2(acc, dp, bq, se, xs, lane, hf);
+    };
+    for (int b = 0; b < nb; b += 2) {
+      if (b + 1 < nb) dma_block(b + 1, sQ1, sD1, sL1, sE1, sB1);
+      blk(sQ0, sD0, sE0);
+      dma_wait();
+      __syncthreads();
+      if (b + 1 >= nb) break;
+      if (b + 2 < nb) dma_block(b + 2, sQ0, sD0, sL0, sE0, sB0);
+      blk(sQ1, sD1, sE1);
+      dma_wait();
+      __syncthreads();
+    }
   }
 
   if (!kvalid) return;
-  u16 *DK = static_cast<u16 *>(a.dk);
-  u16 *DV = static_cast<u16 *>(a.dv);
-  const float sc = a.scale;
+  u16 *OUT = static_cast<u16 *>(role ? a.dk : a.dv);
+  const float sc = role ? a.scale : 1.f;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d0 = 32 * dt + 8 * a4 + 4 * hf;
-      u32x2 wk, wv;
-      wk.x = cvt_pk_bf16(adk[dt][4 * a4 + 0] * sc, adk[dt][4 * a4 + 1] * sc);
-      wk.y = cvt_pk_bf16(adk[dt][4 * a4 + 2] * sc, adk[dt][4 * a4 + 3] * sc);
-      wv.x = cvt_pk_bf16(adv[dt][4 * a4 + 0], adv[dt][4 * a4 + 1]);
-      wv.y = cvt_pk_bf16(adv[dt][4 * a4 + 2], adv[dt][4 * a4 + 3]);
-      *reinterpret_cast<u32x2 *>(DK + koff + d0) = wk;
-      *reinterpret_cast<u32x2 *>(DV + koff + d0) = wv;
+      u32x2 w;
+      w.x = cvt_pk_bf16(acc[dt][4 * a4 + 0] * sc, acc[dt][4 * a4 + 1] * sc);
+      w.y = cvt_pk_bf16(acc[dt][4 * a4 + 2] * sc, acc[dt][4 * a4 + 3] * sc);
+      *reinterpret_cast<u32x2 *>(OUT + koff + d0) = w;
     }
 }
 
@@ -360,7 +440,7 @@ hipError_t launch_bwd_dq_bf16(const BwdDqArgs &a, int n_tiles, hipStream_t s) {
 
 hipError_t launch_bwd_dkdv_bf16(const BwdDkdvArgs &a, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dkdv_bf16_kernel, dim3(n_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dkdv_bf16_kernel, dim3(n_tiles), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

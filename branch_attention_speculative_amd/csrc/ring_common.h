@@ -76,15 +76,15 @@ __device__ __forceinline__ bf16x8 lds_tr(const u16 *X, int k0, int m0, int lane)
 // wave-uniform LDS base + 16 i, so each wave instruction fills 64 consecutive
 // physical chunks (4 rows); lane i of instruction J fills row 4J + i/16,
 // physical chunk i%16, i.e. logical chunk (i%16) ^ swz(row). The 16
-// instructions of a tile are shared by the 4 waves of the workgroup.
+// instructions of a tile are shared by the NW waves of the workgroup.
 // rowaddr(row) gives the global address of a row's first element and must
 // stay in bounds. Completion is tracked by vmcnt: dma_wait() before the
 // barrier that publishes the tile.
-template <class RowAddr>
+template <int NW = 4, class RowAddr>
 __device__ __forceinline__ void dma_tile64(u16 *lds_tile, RowAddr rowaddr, int wave, int lane) {
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int J = wave + 4 * jj;
+  for (int jj = 0; jj < 16 / NW; ++jj) {
+    const int J = wave + NW * jj;
     const int row = 4 * J + (lane >> 4);
     const int c = (lane & 15) ^ swz(row);
     const u16 *src = rowaddr(row) + 8 * c;
