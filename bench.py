@@ -40,9 +40,9 @@ METRIC = "branch-attn fwd+bwd effective TFLOP/s (1 GPU) and % of bf16 MFMA peak"
 # recompute, dO V^T, P^T dO, dS^T Q); the dQ kernel is credited only dS K
 # (its Q K^T and dO V^T recomputes are not counted).
 KERNEL_FLOP_PER_PAIR_D = {"fwd_ring": 4, "bwd_dkdv": 8, "bwd_dq": 2}
-KERNEL_SOURCES = {"fwd_ring": ["fwd_ring.hip", "common.h"],
-                  "bwd_dkdv": ["bwd_ring.hip", "common.h"],
-                  "bwd_dq": ["bwd_ring.hip", "common.h"]}
+KERNEL_SOURCES = {"fwd_ring": ["fwd_ring.hip", "ring_common.h", "common.h"],
+                  "bwd_dkdv": ["bwd_ring.hip", "ring_common.h", "common.h"],
+                  "bwd_dq": ["bwd_ring.hip", "ring_common.h", "common.h"]}
 
 
 def describe(w, info):

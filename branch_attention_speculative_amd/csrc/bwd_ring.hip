@@ -36,15 +36,15 @@ constexpr int kBN = 64;  // keys per block in the dQ kernel
 __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[8],
                                          const bf16x8 (&dreg)[8], const u16 *bk, const u16 *bv,
                                          const Seg &cs, int cj0, int bound, float lse2, float delta,
-                                         float c, int lane, int hf) {
+                                         float c, int hf, const NatOff &no, const TrOff &to) {
   const bool need_mask = cj0 + kBN > cs.n_full;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     f32x16 s = f32x16{}, p = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s = mfma32(lds_nat(bk, 32 * kt, ks * 16, lane), qreg[ks], s);
-      p = mfma32(lds_nat(bv, 32 * kt, ks * 16, lane), dreg[ks], p);
+      s = mfma32(lds_nat_o(bk, 32 * kt, ks, no), qreg[ks], s);
+      p = mfma32(lds_nat_o(bv, 32 * kt, ks, no), dreg[ks], p);
     }
     float ds[16];
 #pragma unroll
@@ -62,7 +62,7 @@ __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[
       const bf16x8 db = pack8(ds + 8 * w);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = mfma32(lds_tr(bk, 32 * kt + 16 * w, 32 * dt, lane), db, acc[dt]);
+        acc[dt] = mfma32(lds_tr_o(bk, 32 * kt + 16 * w, dt, to), db, acc[dt]);
     }
   }
 }
@@ -110,12 +110,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
   const int64_t rs = int64_t(a.hkv) * 128;
   const int g = t.g;
 
+  const NatOff no = nat_offsets(lane);
+  const TrOff to = tr_offsets(lane);
+  const DmaOff<4> dof = dma_offsets<4>(wave, lane, [&](int r) { return int64_t(r) * rs; });
   auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
-    const u16 *kb = K + s.krow * rs + g * 128;
-    const u16 *vb = V + s.krow * rs + g * 128;
-    const int hi = s.n_hi - 1;
-    dma_tile64(dk, [&](int r) { return kb + min(j0 + r, hi) * rs; }, wave, lane);
-    dma_tile64(dv, [&](int r) { return vb + min(j0 + r, hi) * rs; }, wave, lane);
+    const u16 *kb = K + (s.krow + j0) * rs + g * 128;
+    const u16 *vb = V + (s.krow + j0) * rs + g * 128;
+    if (j0 + kBN <= s.n_hi) {
+      dma_tile64_full<4>(dk, kb, dof, wave);
+      dma_tile64_full<4>(dv, vb, dof, wave);
+    } else {  // last block of a chunk: clamp rows to the chunk
+      const int last = s.n_hi - 1 - j0;
+      dma_tile64(dk, [&](int r) { return kb + min(r, last) * rs; }, wave, lane);
+      dma_tile64(dv, [&](int r) { return vb + min(r, last) * rs; }, wave, lane);
+    }
   };
 
   int sg, j0;
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
       const int cj0 = j0;
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
       if (sg < nseg) dma_kv(s, j0, sK1, sV1);
-      if (wave_active) dq_block(acc, qreg, dreg, sK0, sV0, cs, cj0, bound, lse2, delta, c, lane, hf);
+      if (wave_active) dq_block(acc, qreg, dreg, sK0, sV0, cs, cj0, bound, lse2, delta, c, hf, no, to);
       dma_wait();
       __syncthreads();
     }
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
       const int cj0 = j0;
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
       if (sg < nseg) dma_kv(s, j0, sK0, sV0);
-      if (wave_active) dq_block(acc, qreg, dreg, sK1, sV1, cs, cj0, bound, lse2, delta, c, lane, hf);
+      if (wave_active) dq_block(acc, qreg, dreg, sK1, sV1, cs, cj0, bound, lse2, delta, c, hf, no, to);
       dma_wait();
       __syncthreads();
     }
@@ -212,12 +220,13 @@ constexpr int kXchg = 4 * 64 * 4;  // u32 per wave pair: 4 bf16x8 operands x 64 
 template <bool MASK>
 __device__ __forceinline__ void dv_phase1(bf16x8 (&pb)[4], const bf16x8 (&kreg)[8], const u16 *bq,
                                           const float *sl, const int *sb, uint32_t *xs, int nvalid,
-                                          bool kvalid, int kpos, float c, int lane, int hf) {
+                                          bool kvalid, int kpos, float c, int lane, int hf,
+                                          const NatOff &no) {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) s = mfma32(lds_nat(bq, 32 * mt, ks * 16, lane), kreg[ks], s);
+    for (int ks = 0; ks < 8; ++ks) s = mfma32(lds_nat_o(bq, 32 * mt, ks, no), kreg[ks], s);
     float pr[16];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -247,21 +256,21 @@ __device__ __forceinline__ void dv_phase1(bf16x8 (&pb)[4], const bf16x8 (&kreg)[
 
 // dV wave, phase 2: dV^T += dO^T P.
 __device__ __forceinline__ void dv_phase2(f32x16 (&adv)[4], const bf16x8 (&pb)[4], const u16 *bd,
-                                          int lane) {
+                                          const TrOff &to) {
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) adv[dt] = mfma32(lds_tr(bd, 16 * u, 32 * dt, lane), pb[u], adv[dt]);
+    for (int dt = 0; dt < 4; ++dt) adv[dt] = mfma32(lds_tr_o(bd, 16 * u, dt, to), pb[u], adv[dt]);
 }
 
 // dK wave, phase 1: dP = dO V^T for 64 query vectors.
 __device__ __forceinline__ void dk_phase1(f32x16 (&dp)[2], const bf16x8 (&vreg)[8], const u16 *bd,
-                                          int lane) {
+                                          const NatOff &no) {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     f32x16 p = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) p = mfma32(lds_nat(bd, 32 * mt, ks * 16, lane), vreg[ks], p);
+    for (int ks = 0; ks < 8; ++ks) p = mfma32(lds_nat_o(bd, 32 * mt, ks, no), vreg[ks], p);
     dp[mt] = p;
   }
 }
@@ -269,7 +278,8 @@ __device__ __forceinline__ void dk_phase1(f32x16 (&dp)[2], const bf16x8 (&vreg)[
 // dK wave, phase 2: dS = P (dP - Delta) with P from the exchange slot,
 // dK^T += Q^T dS.
 __device__ __forceinline__ void dk_phase2(f32x16 (&adk)[4], const f32x16 (&dp)[2], const u16 *bq,
-                                          const float *sdel, const uint32_t *xs, int lane, int hf) {
+                                          const float *sdel, const uint32_t *xs, int lane, int hf,
+                                          const TrOff &to) {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     float ds[16];
@@ -297,7 +307,7 @@ __device__ __forceinline__ void dk_phase2(f32x16 (&adk)[4], const f32x16 (&dp)[2
       const bf16x8 db = pack8(ds + 8 * w);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        adk[dt] = mfma32(lds_tr(bq, 16 * (2 * mt + w), 32 * dt, lane), db, adk[dt]);
+        adk[dt] = mfma32(lds_tr_o(bq, 16 * (2 * mt + w), dt, to), db, adk[dt]);
     }
   }
 }
@@ -330,17 +340,28 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   const int hq = a.hq;
   uint32_t *xs = sX + (wave & 3) * kXchg;
 
+  const NatOff no = nat_offsets(lane);
+  const TrOff to = tr_offsets(lane);
+  // tile row mq is query vector (row r0 + mq / G, head g G + mq % G)
+  const DmaOff<8> dof = dma_offsets<8>(
+      wave, lane, [&](int mq) { return (int64_t(mq >> log2G) * hq + (mq & (G - 1))) * 128; });
   // issue the loads of inner block b into one buffer set
   auto dma_block = [&](int b, u16 *dq, u16 *dd, float *dl, float *de, int *db) {
     const QBlock qb = qblock(t, b, RB, nb_main);
     const u16 *Q = static_cast<const u16 *>(qb.src ? a.qb : a.q);
     const u16 *DO = static_cast<const u16 *>(qb.src ? a.doutb : a.dout);
     const int hb = t.g * G;
-    auto qrow = [&](int mq) {
-      return (int64_t(min(qb.r0 + (mq >> log2G), qb.hi - 1)) * hq + hb + (mq & (G - 1))) * 128;
-    };
-    dma_tile64<8>(dq, [&](int mq) { return Q + qrow(mq); }, wave, lane);
-    dma_tile64<8>(dd, [&](int mq) { return DO + qrow(mq); }, wave, lane);
+    if (qb.nr == RB) {
+      const int64_t off = (int64_t(qb.r0) * hq + hb) * 128;
+      dma_tile64_full<8>(dq, Q + off, dof, wave);
+      dma_tile64_full<8>(dd, DO + off, dof, wave);
+    } else {  // partial block: clamp rows to the range
+      auto qrow = [&](int mq) {
+        return (int64_t(min(qb.r0 + (mq >> log2G), qb.hi - 1)) * hq + hb + (mq & (G - 1))) * 128;
+      };
+      dma_tile64<8>(dq, [&](int mq) { return Q + qrow(mq); }, wave, lane);
+      dma_tile64<8>(dd, [&](int mq) { return DO + qrow(mq); }, wave, lane);
+    }
     const int64_t base = qb.src ? int64_t(a.n_local) * hq : 0;
     const int rr = min(qb.r0 + (lane >> log2G), qb.hi - 1);
     const int64_t qh = base + int64_t(rr) * hq + hb + (lane & (G - 1));
@@ -377,12 +398,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
       bf16x8 pb[4];
       if (wave_active) {
         if (need_mask(b))
-          dv_phase1<true>(pb, kvreg, bq, sl, sb, xs, nvalid(b), kvalid, kpos, c, lane, hf);
+          dv_phase1<true>(pb, kvreg, bq, sl, sb, xs, nvalid(b), kvalid, kpos, c, lane, hf, no);
         else
-          dv_phase1<false>(pb, kvreg, bq, sl, sb, xs, nvalid(b), kvalid, kpos, c, lane, hf);
+          dv_phase1<false>(pb, kvreg, bq, sl, sb, xs, nvalid(b), kvalid, kpos, c, lane, hf, no);
       }
       __syncthreads();
-      if (wave_active) dv_phase2(acc, pb, bd, lane);
+      if (wave_active) dv_phase2(acc, pb, bd, to);
     };
     for (int b = 0; b < nb; b += 2) {
       if (b + 1 < nb) dma_block(b + 1, sQ1, sD1, sL1, sE1, sB1);
@@ -398,9 +419,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   } else {
     auto blk = [&](const u16 *bq, const u16 *bd, const float *se) {
       f32x16 dp[2];
-      if (wave_active) dk_phase1(dp, kvreg, bd, lane);
+      if (wave_active) dk_phase1(dp, kvreg, bd, no);
       __syncthreads();
-      if (wave_active) dk_phase2(acc, dp, bq, se, xs, lane, hf);
+      if (wave_active) dk_phase2(acc, dp, bq, se, xs, lane, hf, to);
     };
     for (int b = 0; b < nb; b += 2) {
       if (b + 1 < nb) dma_block(b + 1, sQ1, sD1, sL1, sE1, sB1);

@@ -42,13 +42,14 @@ struct FwdState {
 
 // One 64-key block: scores, online softmax update, O += P V.
 __device__ __forceinline__ void fwd_block(FwdState &st, const u16 *bk, const u16 *bv, const Seg &cs,
-                                          int cj0, int bound, float c, int lane, int hf) {
+                                          int cj0, int bound, float c, int hf, const NatOff &no,
+                                          const TrOff &to) {
   // S^T = K Q^T for 64 keys (two 32-key tiles)
   f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    s0 = mfma32(lds_nat(bk, 0, ks * 16, lane), st.qreg[ks], s0);
-    s1 = mfma32(lds_nat(bk, 32, ks * 16, lane), st.qreg[ks], s1);
+    s0 = mfma32(lds_nat_o(bk, 0, ks, no), st.qreg[ks], s0);
+    s1 = mfma32(lds_nat_o(bk, 32, ks, no), st.qreg[ks], s1);
   }
   float x[32];
 #pragma unroll
@@ -91,7 +92,7 @@ __device__ __forceinline__ void fwd_block(FwdState &st, const u16 *bk, const u16
   for (int u = 0; u < 4; ++u) {
     const bf16x8 pb = pack8(x + 8 * u);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.acc[dt] = mfma32(lds_tr(bv, 16 * u, 32 * dt, lane), pb, st.acc[dt]);
+    for (int dt = 0; dt < 4; ++dt) st.acc[dt] = mfma32(lds_tr_o(bv, 16 * u, dt, to), pb, st.acc[dt]);
   }
 }
 
@@ -135,12 +136,20 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
   const int64_t rs = int64_t(a.hkv) * 128;
   const int g = t.g;
 
+  const NatOff no = nat_offsets(lane);
+  const TrOff to = tr_offsets(lane);
+  const DmaOff<4> dof = dma_offsets<4>(wave, lane, [&](int r) { return int64_t(r) * rs; });
   auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
-    const u16 *kb = K + s.krow * rs + g * 128;
-    const u16 *vb = V + s.krow * rs + g * 128;
-    const int last = s.n_hi - 1 - j0;
-    dma_tile64(dk, [&](int r) { return kb + min(j0 + r, j0 + last) * rs; }, wave, lane);
-    dma_tile64(dv, [&](int r) { return vb + min(j0 + r, j0 + last) * rs; }, wave, lane);
+    const u16 *kb = K + (s.krow + j0) * rs + g * 128;
+    const u16 *vb = V + (s.krow + j0) * rs + g * 128;
+    if (j0 + kBN <= s.n_hi) {
+      dma_tile64_full<4>(dk, kb, dof, wave);
+      dma_tile64_full<4>(dv, vb, dof, wave);
+    } else {  // last block of a chunk: clamp rows to the chunk
+      const int last = s.n_hi - 1 - j0;
+      dma_tile64(dk, [&](int r) { return kb + min(r, last) * rs; }, wave, lane);
+      dma_tile64(dv, [&](int r) { return vb + min(r, last) * rs; }, wave, lane);
+    }
   };
 
   int sg, j0;
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
       const int cj0 = j0;
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
       if (sg < nseg) dma_kv(s, j0, sK1, sV1);
-      if (wave_active) fwd_block(st, sK0, sV0, cs, cj0, bound, c, lane, hf);
+      if (wave_active) fwd_block(st, sK0, sV0, cs, cj0, bound, c, hf, no, to);
       dma_wait();
       __syncthreads();
     }
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
       const int cj0 = j0;
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
       if (sg < nseg) dma_kv(s, j0, sK0, sV0);
-      if (wave_active) fwd_block(st, sK1, sV1, cs, cj0, bound, c, lane, hf);
+      if (wave_active) fwd_block(st, sK1, sV1, cs, cj0, bound, c, hf, no, to);
       dma_wait();
       __syncthreads();
     }

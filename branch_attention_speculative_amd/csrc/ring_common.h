@@ -145,4 +145,84 @@ __device__ __forceinline__ void next_block(int &sg, int &j0, Seg &s, const QTile
   }
 }
 
+// ---- precomputed per-lane offsets ----------------------------------------
+// swz(r) only depends on r & 15, so shifting a tile row by a multiple of 16
+// moves every address by a constant. The byte offsets below are computed
+// once per kernel; the reads then add only compile-time immediates.
+
+// lds_nat with row0 = 0: byte offset for each of the 8 column steps ks.
+struct NatOff {
+  int o[8];
+};
+__device__ __forceinline__ NatOff nat_offsets(int lane) {
+  NatOff r;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) r.o[ks] = 2 * toff(lane & 31, 16 * ks + 8 * (lane >> 5));
+  return r;
+}
+// natural operand: rows row0 + (lane & 31), columns 16 ks + 8 (lane / 32) ..
+// (row0 a multiple of 16)
+__device__ __forceinline__ bf16x8 lds_nat_o(const u16 *X, int row0, int ks, const NatOff &no) {
+  return as_bf16x8(*reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(X) + no.o[ks] +
+                                                    row0 * (2 * kRS)));
+}
+
+// lds_tr with k0 = 0: byte offsets of the two reads for each 32-column step dt.
+struct TrOff {
+  int o[2][4];
+};
+__device__ __forceinline__ TrOff tr_offsets(int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int mb = (g & 1) << 4, h = g >> 1;
+  TrOff r;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      r.o[q][dt] = 2 * toff(4 * h + (i >> 2) + 8 * q, 32 * dt + mb + 4 * (i & 3));
+  return r;
+}
+// transposed operand with rows k0 .. k0 + 15 (k0 a multiple of 16), columns
+// 32 dt .. 32 dt + 31 (see lds_tr)
+__device__ __forceinline__ bf16x8 lds_tr_o(const u16 *X, int k0, int dt, const TrOff &to) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const char *base = reinterpret_cast<const char *>(X) + k0 * (2 * kRS);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + to.o[0][dt]));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + to.o[1][dt]));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Direct tile load of 64 rows whose addresses are base + rowoff(row): the
+// per-lane part of the address is fixed for the kernel (DmaOff), only the
+// wave-uniform base changes from tile to tile.
+template <int NW>
+struct DmaOff {
+  uint32_t o[16 / NW];  // byte offsets from the tile base, one per instruction
+};
+// rowoff(row): element offset of tile row `row` from the tile base.
+template <int NW, class RowOff>
+__device__ __forceinline__ DmaOff<NW> dma_offsets(int wave, int lane, RowOff rowoff) {
+  DmaOff<NW> r;
+#pragma unroll
+  for (int jj = 0; jj < 16 / NW; ++jj) {
+    const int J = wave + NW * jj;
+    const int row = 4 * J + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);
+    r.o[jj] = uint32_t((int64_t(rowoff(row)) + 8 * c) * 2);
+  }
+  return r;
+}
+template <int NW>
+__device__ __forceinline__ void dma_tile64_full(u16 *lds_tile, const u16 *base, const DmaOff<NW> &d,
+                                                int wave) {
+#pragma unroll
+  for (int jj = 0; jj < 16 / NW; ++jj) {
+    const int J = wave + NW * jj;
+    const char *src = reinterpret_cast<const char *>(base) + d.o[jj];
+    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lds_tile + 512 * J), 16, 0, 0);
+  }
+}
+
 }  // namespace ba
