@@ -19,7 +19,7 @@ Definitions followed (pages of arXiv:2609.07108):
   gradients locally.
 
 Visible key set V(q) of a query row (the plain definition this module writes
-out; readings in DESIGN.md):
+out, with the readings taken where the pages are silent):
 
 * real main row at position p of sequence s: main keys of s at 0..p;
 * branch row j of an anchor at position pa (branch length n): main keys of s

@@ -11,7 +11,7 @@ Definitions followed (pages of arXiv:2609.07108):
 * ai.info summary, Key Contributions 1 and Methodology: the branch-local part
   lives on the rank that owns the branch's anchor.
 
-Readings where the pages are silent (each one listed in the design doc):
+Readings where the pages are silent:
 
 * every sequence is padded at its tail to a multiple of 2C and cut into 2C
   equal chunks; rank r holds chunks r and 2C-1-r, in that order, sequences in
