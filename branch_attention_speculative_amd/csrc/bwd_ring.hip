@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
 
   const QTile t = a.qtiles[blockIdx.x];
   if (t.nrows == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform_int(tid >> 6);
   const int qi = lane & 31, hf = lane >> 5;
   const int m = wave * 32 + qi;
   const int rl = m >> a.log2G, hh = m & (a.G - 1);
@@ -113,18 +113,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
   const NatOff no = nat_offsets(lane);
   const TrOff to = tr_offsets(lane);
   const DmaOff<4> dof = dma_offsets<4>(wave, lane, [&](int r) { return int64_t(r) * rs; });
+  // K/V rows j0 .. j0 + 63 of a chunk; rows past the chunk's visible end
+  // are not read (their P is masked to zero)
   auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
-    const u16 *kb = K + (s.krow + j0) * rs + g * 128;
-    const u16 *vb = V + (s.krow + j0) * rs + g * 128;
-    if (j0 + kBN <= s.n_hi) {
-      dma_tile64_full<4>(dk, kb, dof, wave);
-      dma_tile64_full<4>(dv, vb, dof, wave);
-    } else {  // last block of a chunk: clamp rows to the chunk
-      const int last = s.n_hi - 1 - j0;
-      dma_tile64(dk, [&](int r) { return kb + min(r, last) * rs; }, wave, lane);
-      dma_tile64(dv, [&](int r) { return vb + min(r, last) * rs; }, wave, lane);
-    }
+    const int64_t off = (s.krow + j0) * rs + g * 128;
+    const uint32_t bytes = uint32_t(((min(kBN, s.n_hi - j0) - 1) * rs + 128) * 2);
+    dma_tile64_buf<4>(dk, buf_rsrc(K + off, bytes), dof, wave);
+    dma_tile64_buf<4>(dv, buf_rsrc(V + off, bytes), dof, wave);
   };
+
+  lds_zero(sK0, kBN * kRS, tid, 256);
+  lds_zero(sV0, kBN * kRS, tid, 256);
+  lds_zero(sK1, kBN * kRS, tid, 256);
+  lds_zero(sV1, kBN * kRS, tid, 256);
+  __syncthreads();
 
   int sg, j0;
   Seg s;
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
 
   const KTile t = a.ktiles[blockIdx.x];
   if (t.nkeys == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform_int(tid >> 6);
   const int role = wave >> 2;  // 0: S, P, dV wave; 1: dP, dS, dK wave
   const int qi = lane & 31, hf = lane >> 5;
   const int kk = (wave & 3) * 32 + qi;  // this lane's key inside the tile
@@ -351,17 +353,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     const u16 *Q = static_cast<const u16 *>(qb.src ? a.qb : a.q);
     const u16 *DO = static_cast<const u16 *>(qb.src ? a.doutb : a.dout);
     const int hb = t.g * G;
-    if (qb.nr == RB) {
-      const int64_t off = (int64_t(qb.r0) * hq + hb) * 128;
-      dma_tile64_full<8>(dq, Q + off, dof, wave);
-      dma_tile64_full<8>(dd, DO + off, dof, wave);
-    } else {  // partial block: clamp rows to the range
-      auto qrow = [&](int mq) {
-        return (int64_t(min(qb.r0 + (mq >> log2G), qb.hi - 1)) * hq + hb + (mq & (G - 1))) * 128;
-      };
-      dma_tile64<8>(dq, [&](int mq) { return Q + qrow(mq); }, wave, lane);
-      dma_tile64<8>(dd, [&](int mq) { return DO + qrow(mq); }, wave, lane);
-    }
+    // query vectors past the range are not read (their P is masked to zero)
+    const int64_t off = (int64_t(qb.r0) * hq + hb) * 128;
+    const uint32_t bytes = uint32_t(((int64_t(qb.nr - 1) * hq + G - 1) * 128 + 128) * 2);
+    dma_tile64_buf<8>(dq, buf_rsrc(Q + off, bytes), dof, wave);
+    dma_tile64_buf<8>(dd, buf_rsrc(DO + off, bytes), dof, wave);
     const int64_t base = qb.src ? int64_t(a.n_local) * hq : 0;
     const int rr = min(qb.r0 + (lane >> log2G), qb.hi - 1);
     const int64_t qh = base + int64_t(rr) * hq + hb + (lane & (G - 1));
@@ -386,6 +382,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+  lds_zero(sQ0, kQB * kRS, tid, 512);
+  lds_zero(sD0, kQB * kRS, tid, 512);
+  lds_zero(sQ1, kQB * kRS, tid, 512);
+  lds_zero(sD1, kQB * kRS, tid, 512);
+  __syncthreads();
 
   // Every block: phase 1, a barrier that publishes P, phase 2, then the
   // barrier that publishes the next block's tiles. The two roles run their

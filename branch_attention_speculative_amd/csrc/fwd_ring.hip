@@ -68,7 +68,7 @@ __device__ __forceinline__ void fwd_block(FwdState &st, const u16 *bk, const u16
   float bmax = x[0];
 #pragma unroll
   for (int v = 1; v < 32; ++v) bmax = fmaxf(bmax, x[v]);
-  bmax = fmaxf(bmax, wave_shfl_xor32(bmax));
+  bmax = xhalf_max(bmax);
   const float cand = bmax * c;
   const bool up = cand > st.mrun + kLazyMax;
   if (__any(up)) {
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
 
   const QTile t = a.qtiles[blockIdx.x];
   if (t.nrows == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform_int(tid >> 6);
   const int qi = lane & 31, hf = lane >> 5;
   const int m = wave * 32 + qi;
   const int rl = m >> a.log2G, hh = m & (a.G - 1);
@@ -139,18 +139,20 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
   const NatOff no = nat_offsets(lane);
   const TrOff to = tr_offsets(lane);
   const DmaOff<4> dof = dma_offsets<4>(wave, lane, [&](int r) { return int64_t(r) * rs; });
+  // K/V rows j0 .. j0 + 63 of a chunk; rows past the chunk's visible end
+  // are not read (their scores are masked)
   auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
-    const u16 *kb = K + (s.krow + j0) * rs + g * 128;
-    const u16 *vb = V + (s.krow + j0) * rs + g * 128;
-    if (j0 + kBN <= s.n_hi) {
-      dma_tile64_full<4>(dk, kb, dof, wave);
-      dma_tile64_full<4>(dv, vb, dof, wave);
-    } else {  // last block of a chunk: clamp rows to the chunk
-      const int last = s.n_hi - 1 - j0;
-      dma_tile64(dk, [&](int r) { return kb + min(r, last) * rs; }, wave, lane);
-      dma_tile64(dv, [&](int r) { return vb + min(r, last) * rs; }, wave, lane);
-    }
+    const int64_t off = (s.krow + j0) * rs + g * 128;
+    const uint32_t bytes = uint32_t(((min(kBN, s.n_hi - j0) - 1) * rs + 128) * 2);
+    dma_tile64_buf<4>(dk, buf_rsrc(K + off, bytes), dof, wave);
+    dma_tile64_buf<4>(dv, buf_rsrc(V + off, bytes), dof, wave);
   };
+
+  lds_zero(sK0, kBN * kRS, tid, 256);
+  lds_zero(sV0, kBN * kRS, tid, 256);
+  lds_zero(sK1, kBN * kRS, tid, 256);
+  lds_zero(sV1, kBN * kRS, tid, 256);
+  __syncthreads();
 
   int sg, j0;
   Seg s;
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
   }
 
   if (!valid) return;
-  const float ltot = st.lsum + wave_shfl_xor32(st.lsum);
+  const float ltot = xhalf_sum(st.lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   const float lse = ltot > 0.f ? (st.mrun + log2f(ltot)) * kLn2 : kNegInf;
   const int64_t ob = (int64_t(row) * a.hq + h) * 128;

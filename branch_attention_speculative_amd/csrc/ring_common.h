@@ -99,6 +99,32 @@ __device__ __forceinline__ void dma_dword64(void *lds_dst, const void *src_lane)
 
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Value of lane 0, held in a scalar register (the argument must be uniform).
+__device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Max / sum of a value over lanes l and l ^ 32 (v_permlane32_swap exchanges
+// the upper half of one register with the lower half of the other; with the
+// same value in both, each lane ends up with its partner's value in one of
+// the two results and its own in the other).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource over the bytes [base, base + bytes). Loads at offsets at or
+// beyond `bytes` return zeros instead of touching memory, which is how the
+// tile loads below stop at the end of a chunk or row range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // ---- ring walk ------------------------------------------------------------
 
 struct Seg {
@@ -214,15 +240,23 @@ __device__ __forceinline__ DmaOff<NW> dma_offsets(int wave, int lane, RowOff row
   }
   return r;
 }
+// Tile load through a buffer resource whose base is the tile's first row:
+// no per-lane address arithmetic, and rows whose offset lies past the
+// resource's extent are not read (zeros). `wave` must be uniform.
 template <int NW>
-__device__ __forceinline__ void dma_tile64_full(u16 *lds_tile, const u16 *base, const DmaOff<NW> &d,
-                                                int wave) {
+__device__ __forceinline__ void dma_tile64_buf(u16 *lds_tile, __amdgpu_buffer_rsrc_t rs,
+                                               const DmaOff<NW> &d, int wave) {
 #pragma unroll
   for (int jj = 0; jj < 16 / NW; ++jj) {
     const int J = wave + NW * jj;
-    const char *src = reinterpret_cast<const char *>(base) + d.o[jj];
-    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(lds_tile + 512 * J), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(lds_tile + 512 * J), 16, d.o[jj], 0, 0, 0);
   }
+}
+
+// Zero `n` u16 of LDS (n a multiple of 8 * nthreads), so that tile rows a
+// load leaves out hold finite values.
+__device__ __forceinline__ void lds_zero(u16 *p, int n, int tid, int nthreads) {
+  for (int i = 8 * tid; i < n; i += 8 * nthreads) *reinterpret_cast<u32x4 *>(p + i) = u32x4{0, 0, 0, 0};
 }
 
 }  // namespace ba
