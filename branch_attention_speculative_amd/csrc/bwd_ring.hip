@@ -35,12 +35,14 @@ constexpr int kBN = 64;  // keys per block in the dQ kernel
 // dS = P (dP - Delta), dQ^T += K^T dS^T.
 __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[8],
                                          const bf16x8 (&dreg)[8], const u16 *bk, const u16 *bv,
-                                         const Seg &cs, int cj0, int bound, float lse2, float delta,
-                                         float c, int hf, const NatOff &no, const TrOff &to) {
+                                         const Seg &cs, int cj0, int bound, float lse2,
+                                         const f32x16 &ndelta, float c, int hf, const NatOff &no,
+                                         const TrOff &to) {
   const bool need_mask = cj0 + kBN > cs.n_full;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    f32x16 s = f32x16{}, p = f32x16{};
+    // dP^T accumulates onto -Delta, so it comes out as dP - Delta
+    f32x16 s = f32x16{}, p = ndelta;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       s = mfma32(lds_nat_o(bk, 32 * kt, ks, no), qreg[ks], s);
@@ -55,7 +57,7 @@ __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[
         const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
         pv = vis ? pv : 0.f;
       }
-      ds[v] = pv * (p[v] - delta);
+      ds[v] = pv * p[v];
     }
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
@@ -67,7 +69,9 @@ __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[
   }
 }
 
-__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
+constexpr int kDqWaves = 8;  // waves per dQ workgroup (32 query vectors each)
+
+__global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sK0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sV0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sK1[kBN * kRS];
@@ -112,20 +116,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
 
   const NatOff no = nat_offsets(lane);
   const TrOff to = tr_offsets(lane);
-  const DmaOff<4> dof = dma_offsets<4>(wave, lane, [&](int r) { return int64_t(r) * rs; });
+  const DmaOff<kDqWaves> dof =
+      dma_offsets<kDqWaves>(wave, lane, [&](int r) { return int64_t(r) * rs; });
   // K/V rows j0 .. j0 + 63 of a chunk; rows past the chunk's visible end
   // are not read (their P is masked to zero)
   auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
     const int64_t off = (s.krow + j0) * rs + g * 128;
     const uint32_t bytes = uint32_t(((min(kBN, s.n_hi - j0) - 1) * rs + 128) * 2);
-    dma_tile64_buf<4>(dk, buf_rsrc(K + off, bytes), dof, wave);
-    dma_tile64_buf<4>(dv, buf_rsrc(V + off, bytes), dof, wave);
+    dma_tile64_buf<kDqWaves>(dk, buf_rsrc(K + off, bytes), dof, wave);
+    dma_tile64_buf<kDqWaves>(dv, buf_rsrc(V + off, bytes), dof, wave);
   };
+  f32x16 ndelta;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ndelta[v] = -delta;
 
-  lds_zero(sK0, kBN * kRS, tid, 256);
-  lds_zero(sV0, kBN * kRS, tid, 256);
-  lds_zero(sK1, kBN * kRS, tid, 256);
-  lds_zero(sV1, kBN * kRS, tid, 256);
+  lds_zero(sK0, kBN * kRS, tid, kDqWaves * 64);
+  lds_zero(sV0, kBN * kRS, tid, kDqWaves * 64);
+  lds_zero(sK1, kBN * kRS, tid, kDqWaves * 64);
+  lds_zero(sV1, kBN * kRS, tid, kDqWaves * 64);
   __syncthreads();
 
   int sg, j0;
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
       const int cj0 = j0;
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
       if (sg < nseg) dma_kv(s, j0, sK1, sV1);
-      if (wave_active) dq_block(acc, qreg, dreg, sK0, sV0, cs, cj0, bound, lse2, delta, c, hf, no, to);
+      if (wave_active) dq_block(acc, qreg, dreg, sK0, sV0, cs, cj0, bound, lse2, ndelta, c, hf, no, to);
       dma_wait();
       __syncthreads();
     }
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdDqArgs a) {
       const int cj0 = j0;
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
       if (sg < nseg) dma_kv(s, j0, sK0, sV0);
-      if (wave_active) dq_block(acc, qreg, dreg, sK1, sV1, cs, cj0, bound, lse2, delta, c, hf, no, to);
+      if (wave_active) dq_block(acc, qreg, dreg, sK1, sV1, cs, cj0, bound, lse2, ndelta, c, hf, no, to);
       dma_wait();
       __syncthreads();
     }
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
 
 hipError_t launch_bwd_dq_bf16(const BwdDqArgs &a, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dq_bf16_kernel, dim3(n_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dq_bf16_kernel, dim3(n_tiles), dim3(kDqWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,28 +1,36 @@
 // Ring-step causal partial, forward (bf16 in, fp32 accumulate, D = 128).
 //
-// One workgroup owns a query tile: up to 128 query vectors (consecutive rows
-// of one sequence chunk x the G q-heads of one kv-head). It walks the virtual
-// ring i = 0..C-1 over shard (r - i) mod C -- the K/V that would circulate
-// while the queries stay (ai.info summary, Methodology; rainbus analysis,
-// method steps, step two) -- and inside each shard the sequence's head chunk,
-// then its tail chunk, in blocks of 64 keys. The online-softmax state
-// (running max, sum, unnormalised O) is carried in registers across blocks
-// and ring steps, which is the log-sum-exp merge between ring steps (rainbus
-// analysis, core method, Eq. 2, applied incrementally). Key blocks past a
-// tile's largest causal bound are never visited; blocks wholly inside its
-// smallest bound skip the mask.
+// One workgroup (8 waves) owns a query tile: up to 256 query vectors
+// (consecutive rows of one sequence chunk x the G q-heads of one kv-head). It
+// walks the virtual ring i = 0..C-1 over shard (r - i) mod C -- the K/V that
+// would circulate while the queries stay (ai.info summary, Methodology;
+// rainbus analysis, method steps, step two) -- and inside each shard the
+// sequence's head chunk, then its tail chunk, in blocks of 64 keys. The
+// online-softmax state (running max, sum, unnormalised O) is carried in
+// registers across blocks and ring steps, which is the log-sum-exp merge
+// between ring steps (rainbus analysis, core method, Eq. 2, applied
+// incrementally). Key blocks past a tile's largest causal bound are never
+// visited; blocks wholly inside its smallest bound skip the mask.
 //
 // Per wave: 32 query vectors. Scores are formed transposed, S^T = K Q^T, so a
-// lane owns one query: the row max and sum need one cross-half exchange and
-// the O rescale is a scalar per lane. O^T += V^T P^T takes P^T straight from
-// the score registers; V^T is read from the row-major V tile with the LDS
+// lane owns one query; O^T += V^T P^T takes P^T straight from the score
+// registers, and V^T is read from the row-major V tile with the LDS
 // transpose read, in the key order the score registers come in.
 //
-// Pipelining: K/V tiles are double-buffered in LDS and the next block is
-// loaded straight from global memory into the idle buffer while the current
-// one is computed (one barrier per block). The running max is only raised when a block's max exceeds it by
-// more than 2^8 (in exp2 units), so most blocks skip the O rescale; the
-// exponentials stay below 2^8 and the final normalisation uses the same max.
+// Vector-unit work is the scarce resource next to the matrix cores (on
+// gfx950 the two do not overlap on a SIMD: every vector instruction costs
+// matrix-core time), so the softmax keeps it to about three and a half
+// instructions per score (scale-and-subtract, exp2, add, half a pack): the
+// running max is the exact max of the first block only and afterwards moves
+// only when a block's exponentials overflow 2^64 (checked once per block on
+// their sum; that block is then redone with its exact max). The sum of P
+// stays in fp32: summing the bf16-rounded P would cost the LSE up to 2^-9
+// relative on rows that see few keys.
+//
+// K and V tiles are double-buffered in LDS and the next block is loaded
+// straight from global memory into the idle buffers while the current one
+// is computed (one barrier per block). Eight waves share each tile, which
+// halves the tile traffic into LDS per product compared with four.
 
 #include "kernels.h"
 #include "ring_common.h"
@@ -31,8 +39,8 @@ namespace ba {
 
 namespace {
 
-constexpr int kBN = 64;          // keys per block
-constexpr float kLazyMax = 8.f;  // rescale threshold (log2 units)
+constexpr int kBN = 64;  // keys per block
+constexpr float kOver = 18446744073709551616.f;  // 2^64: largest sum of P per lane and block
 
 struct FwdState {
   bf16x8 qreg[8];
@@ -40,68 +48,94 @@ struct FwdState {
   float mrun, lsum;
 };
 
-// One 64-key block: scores, online softmax update, O += P V.
-__device__ __forceinline__ void fwd_block(FwdState &st, const u16 *bk, const u16 *bv, const Seg &cs,
-                                          int cj0, int bound, float c, int hf, const NatOff &no,
-                                          const TrOff &to) {
-  // S^T = K Q^T for 64 keys (two 32-key tiles)
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
+// Block of the ring walk: segment sg (with its chunk info) and first key j0
+// inside the chunk.
+struct Blk {
+  int sg, j0;
+  Seg s;
+};
+
+// What the block loop needs of a block.
+struct BlkRec {
+  int64_t off;     // element offset of its first key row (kv-head included)
+  uint32_t bytes;  // extent of its visible rows in bytes; 0: no such block
+  int lim;         // last key of the block any row of the tile sees
+  int pos0;        // sequence position of its first key
+  int need;        // some row of the tile does not see every key of it
+};
+
+// Scores of one 64-key block: two 32-key MFMA tiles; element v of the block
+// is x[v / 16][v % 16].
+typedef f32x16 Scores[2];
+
+// S^T = K Q^T for one 64-key block.
+__device__ __forceinline__ void scores(Scores &x, const u16 *bk, const FwdState &st,
+                                       const NatOff &no) {
+  x[0] = f32x16{};
+  x[1] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    s0 = mfma32(lds_nat_o(bk, 0, ks, no), st.qreg[ks], s0);
-    s1 = mfma32(lds_nat_o(bk, 32, ks, no), st.qreg[ks], s1);
-  }
-  float x[32];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    x[v] = s0[v];
-    x[16 + v] = s1[v];
-  }
-  if (cj0 + kBN > cs.n_full) {
-#pragma unroll
-    for (int v = 0; v < 32; ++v) {
-      const int jj = cj0 + 32 * (v >> 4) + 8 * ((v & 15) >> 2) + 4 * hf + (v & 3);
-      const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
-      x[v] = vis ? x[v] : kNegInf;
-    }
-  }
-  float bmax = x[0];
-#pragma unroll
-  for (int v = 1; v < 32; ++v) bmax = fmaxf(bmax, x[v]);
-  bmax = xhalf_max(bmax);
-  const float cand = bmax * c;
-  const bool up = cand > st.mrun + kLazyMax;
-  if (__any(up)) {
-    const float mnew = up ? cand : st.mrun;
-    const float alpha = (mnew == st.mrun) ? 1.f : fast_exp2(st.mrun - mnew);
-    st.mrun = mnew;
-    st.lsum *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.acc[dt] *= alpha;
-  }
-  const float mu = (st.mrun == kNegInf) ? 0.f : st.mrun;
-  float psum = 0.f;
-#pragma unroll
-  for (int v = 0; v < 32; ++v) {
-    x[v] = fast_exp2(fmaf(x[v], c, -mu));
-    psum += x[v];
-  }
-  st.lsum += psum;
-  // O^T += V^T P^T
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const bf16x8 pb = pack8(x + 8 * u);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.acc[dt] = mfma32(lds_tr_o(bv, 16 * u, dt, to), pb, st.acc[dt]);
+    x[0] = mfma32(lds_nat_o(bk, 0, ks, no), st.qreg[ks], x[0]);
+    x[1] = mfma32(lds_nat_o(bk, 32, ks, no), st.qreg[ks], x[1]);
   }
 }
 
-__global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
-  // double-buffered K/V tiles; separate objects so the LDS loads into one
-  // buffer never order the reads of the other
+// Scores past the chunk's visible end or past this lane's causal bound get
+// -inf. lim = last visible key of the block for this lane's half (relative
+// to the block start, minus 4 hf).
+__device__ __forceinline__ void mask_block(Scores &x, int lim) {
+#pragma unroll
+  for (int v = 0; v < 32; ++v) {
+    const int jj = 32 * (v >> 4) + 8 * ((v & 15) >> 2) + (v & 3);
+    x[v >> 4][v & 15] = jj <= lim ? x[v >> 4][v & 15] : kNegInf;
+  }
+}
+
+__device__ __forceinline__ float block_max(const Scores &x) {
+  float m0 = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]), m1 = fmaxf(fmaxf(x[1][0], x[1][1]), x[1][2]);
+#pragma unroll
+  for (int v = 3; v < 15; v += 2) {
+    m0 = fmaxf(fmaxf(m0, x[0][v]), x[0][v + 1]);
+    m1 = fmaxf(fmaxf(m1, x[1][v]), x[1][v + 1]);
+  }
+  m0 = fmaxf(m0, x[0][15]);
+  m1 = fmaxf(m1, x[1][15]);
+  return xhalf_max(fmaxf(m0, m1));
+}
+
+// P = exp2(c S - mu) packed to bf16, and its per-lane sum in fp32.
+__device__ __forceinline__ float exp_block(bf16x8 (&pb)[4], const Scores &x, float c, float mu) {
+  float psum = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      e[i] = fast_exp2(fmaf(x[u >> 1][8 * (u & 1) + i], c, -mu));
+      psum += e[i];
+    }
+    pb[u] = pack8(e);
+  }
+  return psum;
+}
+
+// O^T += V^T P^T.
+__device__ __forceinline__ void pv_block(FwdState &st, const bf16x8 (&pb)[4], const u16 *bv,
+                                         const TrOff &to) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.acc[dt] = mfma32(lds_tr_o(bv, 16 * u, dt, to), pb[u], st.acc[dt]);
+}
+
+constexpr int kWaves = 8;  // waves per workgroup, 32 query vectors each
+
+__global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingArgs a) {
+  // two K and two V tiles; separate objects so the LDS loads into one
+  // buffer never order the reads of another
   __shared__ __attribute__((aligned(16))) u16 sK0[kBN * kRS];
-  __shared__ __attribute__((aligned(16))) u16 sV0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sK1[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sV0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sV1[kBN * kRS];
 
   const QTile t = a.qtiles[blockIdx.x];
@@ -130,56 +164,95 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
   }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) st.acc[dt] = f32x16{};
-  st.mrun = kNegInf;
+  st.mrun = 0.f;
   st.lsum = 0.f;
   const float c = a.scale_log2;
   const int64_t rs = int64_t(a.hkv) * 128;
   const int g = t.g;
+  const int C = a.C, r = a.r, n_local = a.n_local, nseg = 2 * C;
 
   const NatOff no = nat_offsets(lane);
   const TrOff to = tr_offsets(lane);
-  const DmaOff<4> dof = dma_offsets<4>(wave, lane, [&](int r) { return int64_t(r) * rs; });
-  // K/V rows j0 .. j0 + 63 of a chunk; rows past the chunk's visible end
-  // are not read (their scores are masked)
-  auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
-    const int64_t off = (s.krow + j0) * rs + g * 128;
-    const uint32_t bytes = uint32_t(((min(kBN, s.n_hi - j0) - 1) * rs + 128) * 2);
-    dma_tile64_buf<4>(dk, buf_rsrc(K + off, bytes), dof, wave);
-    dma_tile64_buf<4>(dv, buf_rsrc(V + off, bytes), dof, wave);
+  const DmaOff<kWaves> dof =
+      dma_offsets<kWaves>(wave, lane, [&](int rr) { return int64_t(rr) * rs; });
+  auto rec = [&](const Blk &b) {
+    BlkRec q;
+    if (b.sg >= nseg) {
+      q.off = 0;
+      q.bytes = 0;
+      q.lim = q.pos0 = q.need = 0;
+      return q;
+    }
+    q.off = (b.s.krow + b.j0) * rs + g * 128;
+    q.lim = min(kBN, b.s.n_hi - b.j0) - 1;
+    q.bytes = uint32_t((q.lim * rs + 128) * 2);
+    q.pos0 = b.s.cpos0 + b.j0;
+    q.need = b.j0 + kBN > b.s.n_full;
+    return q;
+  };
+  // rows of the block past the chunk's visible end are not read (their
+  // scores are masked)
+  auto load = [&](u16 *dk, u16 *dv, const BlkRec &q) {
+    dma_tile64_buf<kWaves>(dk, buf_rsrc(K + q.off, q.bytes), dof, wave);
+    dma_tile64_buf<kWaves>(dv, buf_rsrc(V + q.off, q.bytes), dof, wave);
   };
 
-  lds_zero(sK0, kBN * kRS, tid, 256);
-  lds_zero(sV0, kBN * kRS, tid, 256);
-  lds_zero(sK1, kBN * kRS, tid, 256);
-  lds_zero(sV1, kBN * kRS, tid, 256);
-  __syncthreads();
+  lds_zero(sK0, kBN * kRS, tid, kWaves * 64);
+  lds_zero(sK1, kBN * kRS, tid, kWaves * 64);
+  lds_zero(sV0, kBN * kRS, tid, kWaves * 64);
+  lds_zero(sV1, kBN * kRS, tid, kWaves * 64);
 
-  int sg, j0;
-  Seg s;
-  first_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
-  const int nseg = 2 * a.C;
-  if (sg < nseg) dma_kv(s, j0, sK0, sV0);
-  dma_wait();
-  __syncthreads();
-  while (sg < nseg) {
-    {
-      const Seg cs = s;
-      const int cj0 = j0;
-      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
-      if (sg < nseg) dma_kv(s, j0, sK1, sV1);
-      if (wave_active) fwd_block(st, sK0, sV0, cs, cj0, bound, c, hf, no, to);
-      dma_wait();
+  Blk wk;  // the walker: one block ahead of the one computed
+  first_block<kBN>(wk.sg, wk.j0, wk.s, t, C, r, n_local);
+  BlkRec cur = rec(wk);
+  if (cur.bytes) {  // else every row of the tile is a pad: O = 0, LSE = -inf
+    next_block<kBN>(wk.sg, wk.j0, wk.s, t, C, r, n_local);
+    __syncthreads();  // LDS zeroed before any tile load lands
+    load(sK0, sV0, cur);
+    vm_wait<0>();
+    bool first = true;
+    // one block: KC/VC hold it, KN/VN receive the next one
+    auto iter = [&](u16 *KC, u16 *VC, u16 *KN, u16 *VN) {
       __syncthreads();
-    }
-    if (sg >= nseg) break;
-    {
-      const Seg cs = s;
-      const int cj0 = j0;
-      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
-      if (sg < nseg) dma_kv(s, j0, sK0, sV0);
-      if (wave_active) fwd_block(st, sK1, sV1, cs, cj0, bound, c, hf, no, to);
-      dma_wait();
-      __syncthreads();
+      const BlkRec nxt = rec(wk);
+      if (nxt.bytes) {
+        load(KN, VN, nxt);
+        next_block<kBN>(wk.sg, wk.j0, wk.s, t, C, r, n_local);
+      }
+      if (wave_active) {
+        Scores x;
+        scores(x, KC, st, no);
+        if (cur.need) mask_block(x, min(cur.lim, bound - cur.pos0) - 4 * hf);
+        if (first) {
+          // every real row sees the first key of the first block
+          const float bm = block_max(x) * c;
+          st.mrun = (bm > kNegInf) ? bm : 0.f;
+        }
+        bf16x8 pb[4];
+        float psum = exp_block(pb, x, c, st.mrun);
+        if (__any(!(psum <= kOver))) {
+          // a score rose far above the running max: raise it to the block's
+          // exact max, rescale, redo the exponentials
+          const float mnew = fmaxf(st.mrun, block_max(x) * c);
+          const float alpha = fast_exp2(st.mrun - mnew);
+          st.mrun = mnew;
+          st.lsum *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) st.acc[dt] *= alpha;
+          psum = exp_block(pb, x, c, st.mrun);
+        }
+        st.lsum += psum;
+        pv_block(st, pb, VC, to);
+      }
+      first = false;
+      cur = nxt;
+      vm_wait<0>();
+    };
+    while (true) {
+      iter(sK0, sV0, sK1, sV1);
+      if (!cur.bytes) break;
+      iter(sK1, sV1, sK0, sV0);
+      if (!cur.bytes) break;
     }
   }
 
@@ -219,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void fwd_ring_bf16_kernel(FwdRingArgs a) {
 
 hipError_t launch_fwd_ring_bf16(const FwdRingArgs &a, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_ring_bf16_kernel, dim3(n_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(fwd_ring_bf16_kernel, dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@
 namespace ba {
 
 // Tiling constants of the bf16 MFMA kernels (D = 128).
-constexpr int kQTileVecs = 128;   // query vectors (row, head) per forward / dQ tile
+constexpr int kQTileVecs = 256;   // query vectors (row, head) per forward / dQ tile
 constexpr int kKTileKeys = 128;   // keys per dK/dV tile
 constexpr int kKBlockVecs = 64;   // query vectors per dK/dV inner block
 constexpr int kMaxBranch = 64;    // longest branch the branch-local kernels accept

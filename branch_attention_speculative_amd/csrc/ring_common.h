@@ -99,6 +99,13 @@ __device__ __forceinline__ void dma_dword64(void *lds_dst, const void *src_lane)
 
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Value of lane 0, held in a scalar register (the argument must be uniform).
 __device__ __forceinline__ int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

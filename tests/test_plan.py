@@ -113,7 +113,7 @@ def _check_worklists(p, lay, br, w):
     for g, src, row0, nrows, seq_off, c, pmin, pmax in qt:
         if nrows == 0:
             continue
-        assert nrows * G <= 128
+        assert nrows * G <= 256
         rows = np.arange(row0, row0 + nrows)
         (seen_b if src else seen_m)[g, rows] += 1
         b = (bound_b if src else bound_m)[rows]
