@@ -217,11 +217,12 @@ __device__ __forceinline__ QBlock qblock(const KTile &t, int b, int RB, int nb_m
 // The eight waves of a dK/dV workgroup come in pairs that own the same 32
 // keys and sit on the same SIMD. The first wave of a pair computes S = Q K^T,
 // P = exp(S - LSE) and dV^T += dO^T P; it also hands P (bf16, in its MFMA
-// register layout) to its partner through LDS. The partner computes
-// dP = dO V^T and, once P is published by a barrier, dS = P (dP - Delta) and
-// dK^T += Q^T dS. Each wave then needs about half the registers of one wave
-// doing all four products, so two waves fit on each SIMD and overlap each
-// other's vector and matrix-core phases, with no duplicated products.
+// register layout) to its partner through LDS. The partner runs one inner
+// block behind: it computes dP = dO V^T and dS = P (dP - Delta) with the P
+// its partner published in the previous block, and dK^T += Q^T dS. Each wave
+// then needs about half the registers of one wave doing all four products,
+// so two waves fit on each SIMD, with no duplicated products and a single
+// barrier per block.
 
 constexpr int kXchg = 4 * 64 * 4;  // u32 per wave pair: 4 bf16x8 operands x 64 lanes
 
@@ -323,13 +324,21 @@ __device__ __forceinline__ void dk_phase2(f32x16 (&adk)[4], const f32x16 (&dp)[2
 }
 
 __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
+  // Q / dO tiles and the per-row LSE, Delta and bounds of an inner block,
+  // three sets: the dV waves work on block b while the dK waves work on
+  // block b - 1 and block b + 1 is loading. Separate objects so the LDS loads
+  // into one set never order the reads of another.
   __shared__ __attribute__((aligned(16))) u16 sQ0[kQB * kRS];
   __shared__ __attribute__((aligned(16))) u16 sD0[kQB * kRS];
   __shared__ __attribute__((aligned(16))) u16 sQ1[kQB * kRS];
   __shared__ __attribute__((aligned(16))) u16 sD1[kQB * kRS];
-  __shared__ __attribute__((aligned(16))) float sL0[kQB], sE0[kQB], sL1[kQB], sE1[kQB];
-  __shared__ __attribute__((aligned(16))) int sB0[kQB], sB1[kQB];
-  __shared__ __attribute__((aligned(16))) uint32_t sX[4 * kXchg];
+  __shared__ __attribute__((aligned(16))) u16 sQ2[kQB * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sD2[kQB * kRS];
+  __shared__ __attribute__((aligned(16))) float sL0[kQB], sE0[kQB], sL1[kQB], sE1[kQB], sL2[kQB],
+      sE2[kQB];
+  __shared__ __attribute__((aligned(16))) int sB0[kQB], sB1[kQB], sB2[kQB];
+  // P exchange, two slots (block parity) per wave pair
+  __shared__ __attribute__((aligned(16))) uint32_t sX[2 * 4 * kXchg];
 
   const KTile t = a.ktiles[blockIdx.x];
   if (t.nkeys == 0) return;
@@ -348,7 +357,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   const int nb_main = (t.qm_end - t.qm_start + RB - 1) / RB;
   const int nb = nb_main + (t.qb_end - t.qb_start + RB - 1) / RB;
   const int hq = a.hq;
-  uint32_t *xs = sX + (wave & 3) * kXchg;
+  uint32_t *xs0 = sX + (wave & 3) * kXchg;  // slot of even blocks
+  uint32_t *xs1 = xs0 + 4 * kXchg;          // slot of odd blocks
 
   const NatOff no = nat_offsets(lane);
   const TrOff to = tr_offsets(lane);
@@ -395,54 +405,62 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   lds_zero(sD0, kQB * kRS, tid, 512);
   lds_zero(sQ1, kQB * kRS, tid, 512);
   lds_zero(sD1, kQB * kRS, tid, 512);
+  lds_zero(sQ2, kQB * kRS, tid, 512);
+  lds_zero(sD2, kQB * kRS, tid, 512);
   __syncthreads();
 
-  // Every block: phase 1, a barrier that publishes P, phase 2, then the
-  // barrier that publishes the next block's tiles. The two roles run their
-  // own loops with the same barrier sequence.
+  // Iteration b = 0 .. nb: one barrier, the loads of block b + 1, then the
+  // dV waves do block b (S, P -> exchange slot b % 2, dV) and the dK waves
+  // do block b - 1 (dP, dS with P from slot (b - 1) % 2, dK). The barrier at
+  // the top of iteration b publishes block b's tiles and P of block b - 1,
+  // and frees the set and slot that iteration b + 1 overwrites.
   if (nb > 0) dma_block(0, sQ0, sD0, sL0, sE0, sB0);
   dma_wait();
-  __syncthreads();
+  // The two roles run separate loops with the same barrier sequence.
   if (role == 0) {
-    auto blk = [&](int b, const u16 *bq, const u16 *bd, const float *sl, const int *sb) {
-      bf16x8 pb[4];
-      if (wave_active) {
+    // block b in the set (Qc, Dc, Lc, Bc); block b + 1 loads into the next set
+    auto iter = [&](int b, const u16 *Qc, const u16 *Dc, const float *Lc, const int *Bc, u16 *Qn,
+                    u16 *Dn, float *Ln, float *En, int *Bn) {
+      __syncthreads();
+      if (b + 1 < nb) dma_block(b + 1, Qn, Dn, Ln, En, Bn);
+      if (wave_active && b < nb) {
+        uint32_t *xs = (b & 1) ? xs1 : xs0;
+        bf16x8 pb[4];
         if (need_mask(b))
-          dv_phase1<true>(pb, kvreg, bq, sl, sb, xs, nvalid(b), kvalid, kpos, c, lane, hf, no);
+          dv_phase1<true>(pb, kvreg, Qc, Lc, Bc, xs, nvalid(b), kvalid, kpos, c, lane, hf, no);
         else
-          dv_phase1<false>(pb, kvreg, bq, sl, sb, xs, nvalid(b), kvalid, kpos, c, lane, hf, no);
+          dv_phase1<false>(pb, kvreg, Qc, Lc, Bc, xs, nvalid(b), kvalid, kpos, c, lane, hf, no);
+        dv_phase2(acc, pb, Dc, to);
       }
-      __syncthreads();
-      if (wave_active) dv_phase2(acc, pb, bd, to);
+      dma_wait();
     };
-    for (int b = 0; b < nb; b += 2) {
-      if (b + 1 < nb) dma_block(b + 1, sQ1, sD1, sL1, sE1, sB1);
-      blk(b, sQ0, sD0, sL0, sB0);
-      dma_wait();
-      __syncthreads();
-      if (b + 1 >= nb) break;
-      if (b + 2 < nb) dma_block(b + 2, sQ0, sD0, sL0, sE0, sB0);
-      blk(b + 1, sQ1, sD1, sL1, sB1);
-      dma_wait();
-      __syncthreads();
+    for (int b = 0; b <= nb; b += 3) {
+      iter(b, sQ0, sD0, sL0, sB0, sQ1, sD1, sL1, sE1, sB1);
+      if (b + 1 > nb) break;
+      iter(b + 1, sQ1, sD1, sL1, sB1, sQ2, sD2, sL2, sE2, sB2);
+      if (b + 2 > nb) break;
+      iter(b + 2, sQ2, sD2, sL2, sB2, sQ0, sD0, sL0, sE0, sB0);
     }
   } else {
-    auto blk = [&](const u16 *bq, const u16 *bd, const float *se) {
-      f32x16 dp[2];
-      if (wave_active) dk_phase1(dp, kvreg, bd, no);
+    // block b - 1 in the set (Qp, Dp, Ep); block b + 1 loads into the next set
+    auto iter = [&](int b, const u16 *Qp, const u16 *Dp, const float *Ep, u16 *Qn, u16 *Dn,
+                    float *Ln, float *En, int *Bn) {
       __syncthreads();
-      if (wave_active) dk_phase2(acc, dp, bq, se, xs, lane, hf, to);
+      if (b + 1 < nb) dma_block(b + 1, Qn, Dn, Ln, En, Bn);
+      if (wave_active && b >= 1) {
+        const uint32_t *xs = (b & 1) ? xs0 : xs1;  // slot of block b - 1
+        f32x16 dp[2];
+        dk_phase1(dp, kvreg, Dp, no);
+        dk_phase2(acc, dp, Qp, Ep, xs, lane, hf, to);
+      }
+      dma_wait();
     };
-    for (int b = 0; b < nb; b += 2) {
-      if (b + 1 < nb) dma_block(b + 1, sQ1, sD1, sL1, sE1, sB1);
-      blk(sQ0, sD0, sE0);
-      dma_wait();
-      __syncthreads();
-      if (b + 1 >= nb) break;
-      if (b + 2 < nb) dma_block(b + 2, sQ0, sD0, sL0, sE0, sB0);
-      blk(sQ1, sD1, sE1);
-      dma_wait();
-      __syncthreads();
+    for (int b = 0; b <= nb; b += 3) {
+      iter(b, sQ2, sD2, sE2, sQ1, sD1, sL1, sE1, sB1);
+      if (b + 1 > nb) break;
+      iter(b + 1, sQ0, sD0, sE0, sQ2, sD2, sL2, sE2, sB2);
+      if (b + 2 > nb) break;
+      iter(b + 2, sQ1, sD1, sE1, sQ0, sD0, sL0, sE0, sB0);
     }
   }
 
