@@ -337,8 +337,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   __shared__ __attribute__((aligned(16))) float sL0[kQB], sE0[kQB], sL1[kQB], sE1[kQB], sL2[kQB],
       sE2[kQB];
   __shared__ __attribute__((aligned(16))) int sB0[kQB], sB1[kQB], sB2[kQB];
-  // P exchange, two slots (block parity) per wave pair
-  __shared__ __attribute__((aligned(16))) uint32_t sX[2 * 4 * kXchg];
+  // P exchange of each wave pair, one slot per set (block b uses slot b % 3)
+  __shared__ __attribute__((aligned(16))) uint32_t sX0[4 * kXchg];
+  __shared__ __attribute__((aligned(16))) uint32_t sX1[4 * kXchg];
+  __shared__ __attribute__((aligned(16))) uint32_t sX2[4 * kXchg];
 
   const KTile t = a.ktiles[blockIdx.x];
   if (t.nkeys == 0) return;
@@ -357,8 +359,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   const int nb_main = (t.qm_end - t.qm_start + RB - 1) / RB;
   const int nb = nb_main + (t.qb_end - t.qb_start + RB - 1) / RB;
   const int hq = a.hq;
-  uint32_t *xs0 = sX + (wave & 3) * kXchg;  // slot of even blocks
-  uint32_t *xs1 = xs0 + 4 * kXchg;          // slot of odd blocks
+  const int xo = (wave & 3) * kXchg;  // this pair's part of an exchange slot
 
   const NatOff no = nat_offsets(lane);
   const TrOff to = tr_offsets(lane);
@@ -383,11 +384,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     if (wave == 2) dma_dword64(de, a.delta + qh);
     if (wave == 3) dma_dword64(db, (qb.src ? a.bound_branch : a.bound_main) + rr);
   };
-  auto need_mask = [&](int b) {
+  // no mask when every row of the block sees every key of the tile; rows
+  // are in increasing bound order, so the first row's bound (sb[0], the
+  // block's bounds in LDS) decides
+  auto need_mask = [&](int b, const int *sb) {
     const QBlock qb = qblock(t, b, RB, nb_main);
-    const int32_t *BOUND = qb.src ? a.bound_branch : a.bound_main;
-    // no mask when every row of the block sees every key of the tile
-    return !(qb.nr == RB && t.nkeys == kKTileKeys && BOUND[qb.r0] >= t.kpos0 + kKTileKeys - 1);
+    return !(qb.nr == RB && t.nkeys == kKTileKeys && sb[0] >= t.kpos0 + kKTileKeys - 1);
   };
   auto nvalid = [&](int b) { return qblock(t, b, RB, nb_main).nr << log2G; };
 
@@ -410,8 +412,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   __syncthreads();
 
   // Iteration b = 0 .. nb: one barrier, the loads of block b + 1, then the
-  // dV waves do block b (S, P -> exchange slot b % 2, dV) and the dK waves
-  // do block b - 1 (dP, dS with P from slot (b - 1) % 2, dK). The barrier at
+  // dV waves do block b (S, P -> exchange slot b % 3, dV) and the dK waves
+  // do block b - 1 (dP, dS with P from slot (b - 1) % 3, dK). The barrier at
   // the top of iteration b publishes block b's tiles and P of block b - 1,
   // and frees the set and slot that iteration b + 1 overwrites.
   if (nb > 0) dma_block(0, sQ0, sD0, sL0, sE0, sB0);
@@ -419,14 +421,15 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   // The two roles run separate loops with the same barrier sequence.
   if (role == 0) {
     // block b in the set (Qc, Dc, Lc, Bc); block b + 1 loads into the next set
-    auto iter = [&](int b, const u16 *Qc, const u16 *Dc, const float *Lc, const int *Bc, u16 *Qn,
-                    u16 *Dn, float *Ln, float *En, int *Bn) {
+    auto iter = [&](int b, const u16 *Qc, const u16 *Dc, const float *Lc, const int *Bc, uint32_t *Xc,
+                    u16 *Qn, u16 *Dn, float *Ln, float *En, int *Bn) {
       __syncthreads();
+      const bool mask = b < nb && need_mask(b, Bc);
       if (b + 1 < nb) dma_block(b + 1, Qn, Dn, Ln, En, Bn);
       if (wave_active && b < nb) {
-        uint32_t *xs = (b & 1) ? xs1 : xs0;
+        uint32_t *xs = Xc + xo;
         bf16x8 pb[4];
-        if (need_mask(b))
+        if (mask)
           dv_phase1<true>(pb, kvreg, Qc, Lc, Bc, xs, nvalid(b), kvalid, kpos, c, lane, hf, no);
         else
           dv_phase1<false>(pb, kvreg, Qc, Lc, Bc, xs, nvalid(b), kvalid, kpos, c, lane, hf, no);
@@ -435,20 +438,20 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
       dma_wait();
     };
     for (int b = 0; b <= nb; b += 3) {
-      iter(b, sQ0, sD0, sL0, sB0, sQ1, sD1, sL1, sE1, sB1);
+      iter(b, sQ0, sD0, sL0, sB0, sX0, sQ1, sD1, sL1, sE1, sB1);
       if (b + 1 > nb) break;
-      iter(b + 1, sQ1, sD1, sL1, sB1, sQ2, sD2, sL2, sE2, sB2);
+      iter(b + 1, sQ1, sD1, sL1, sB1, sX1, sQ2, sD2, sL2, sE2, sB2);
       if (b + 2 > nb) break;
-      iter(b + 2, sQ2, sD2, sL2, sB2, sQ0, sD0, sL0, sE0, sB0);
+      iter(b + 2, sQ2, sD2, sL2, sB2, sX2, sQ0, sD0, sL0, sE0, sB0);
     }
   } else {
     // block b - 1 in the set (Qp, Dp, Ep); block b + 1 loads into the next set
-    auto iter = [&](int b, const u16 *Qp, const u16 *Dp, const float *Ep, u16 *Qn, u16 *Dn,
-                    float *Ln, float *En, int *Bn) {
+    auto iter = [&](int b, const u16 *Qp, const u16 *Dp, const float *Ep, const uint32_t *Xp,
+                    u16 *Qn, u16 *Dn, float *Ln, float *En, int *Bn) {
       __syncthreads();
       if (b + 1 < nb) dma_block(b + 1, Qn, Dn, Ln, En, Bn);
       if (wave_active && b >= 1) {
-        const uint32_t *xs = (b & 1) ? xs0 : xs1;  // slot of block b - 1
+        const uint32_t *xs = Xp + xo;  // P of block b - 1
         f32x16 dp[2];
         dk_phase1(dp, kvreg, Dp, no);
         dk_phase2(acc, dp, Qp, Ep, xs, lane, hf, to);
@@ -456,11 +459,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
       dma_wait();
     };
     for (int b = 0; b <= nb; b += 3) {
-      iter(b, sQ2, sD2, sE2, sQ1, sD1, sL1, sE1, sB1);
+      iter(b, sQ2, sD2, sE2, sX2, sQ1, sD1, sL1, sE1, sB1);
       if (b + 1 > nb) break;
-      iter(b + 1, sQ0, sD0, sE0, sQ2, sD2, sL2, sE2, sB2);
+      iter(b + 1, sQ0, sD0, sE0, sX0, sQ2, sD2, sL2, sE2, sB2);
       if (b + 2 > nb) break;
-      iter(b + 2, sQ1, sD1, sE1, sQ0, sD0, sL0, sE0, sB0);
+      iter(b + 2, sQ1, sD1, sE1, sX1, sQ0, sD0, sL0, sE0, sB0);
     }
   }
 
