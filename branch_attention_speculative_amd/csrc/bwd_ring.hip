@@ -274,12 +274,20 @@ __device__ __forceinline__ void dv_phase2(f32x16 (&adv)[4], const bf16x8 (&pb)[4
     for (int dt = 0; dt < 4; ++dt) adv[dt] = mfma32(lds_tr_o(bd, 16 * u, dt, to), pb[u], adv[dt]);
 }
 
-// dK wave, phase 1: dP = dO V^T for 64 query vectors.
+// dK wave, phase 1: dP - Delta = dO V^T - Delta for 64 query vectors (the
+// product accumulates onto -Delta of each row).
 __device__ __forceinline__ void dk_phase1(f32x16 (&dp)[2], const bf16x8 (&vreg)[8], const u16 *bd,
-                                          const NatOff &no) {
+                                          const float *sdel, int hf, const NatOff &no) {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    f32x16 p = f32x16{};
+    f32x16 p;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // rows 32 mt + 8 g4 + 4 hf + 0..3 are four consecutive slots
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sdel + 32 * mt + 8 * g4 + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[4 * g4 + e] = -d4[e];
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) p = mfma32(lds_nat_o(bd, 32 * mt, ks, no), vreg[ks], p);
     dp[mt] = p;
@@ -289,8 +297,7 @@ __device__ __forceinline__ void dk_phase1(f32x16 (&dp)[2], const bf16x8 (&vreg)[
 // dK wave, phase 2: dS = P (dP - Delta) with P from the exchange slot,
 // dK^T += Q^T dS.
 __device__ __forceinline__ void dk_phase2(f32x16 (&adk)[4], const f32x16 (&dp)[2], const u16 *bq,
-                                          const float *sdel, const uint32_t *xs, int lane, int hf,
-                                          const TrOff &to) {
+                                          const uint32_t *xs, int lane, const TrOff &to) {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     float ds[16];
@@ -304,15 +311,7 @@ __device__ __forceinline__ void dk_phase2(f32x16 (&adk)[4], const f32x16 (&dp)[2
       }
     }
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int q0 = 32 * mt + 8 * g4 + 4 * hf;
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sdel + q0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = 4 * g4 + e;
-        ds[v] = ds[v] * (dp[mt][v] - d4[e]);
-      }
-    }
+    for (int v = 0; v < 16; ++v) ds[v] *= dp[mt][v];
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       const bf16x8 db = pack8(ds + 8 * w);
@@ -453,8 +452,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
       if (wave_active && b >= 1) {
         const uint32_t *xs = Xp + xo;  // P of block b - 1
         f32x16 dp[2];
-        dk_phase1(dp, kvreg, Dp, no);
-        dk_phase2(acc, dp, Qp, Ep, xs, lane, hf, to);
+        dk_phase1(dp, kvreg, Dp, Ep, hf, no);
+        dk_phase2(acc, dp, Qp, xs, lane, to);
       }
       dma_wait();
     };
