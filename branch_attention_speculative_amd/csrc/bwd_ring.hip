@@ -32,13 +32,14 @@ constexpr int kBN = 64;  // keys per block in the dQ kernel
 // dQ: query-stationary ring replay
 
 // One 64-key block, one 32-key tile at a time: S^T = K Q^T, dP^T = V dO^T,
-// dS = P (dP - Delta), dQ^T += K^T dS^T.
+// dS = P (dP - Delta), dQ^T += K^T dS^T. When the block crosses a causal
+// bound or the chunk's visible end (need_mask), scores of keys past lim (the
+// last visible key for this lane, relative to the block, minus 4 hf) are
+// set to -inf before the exponentials.
 __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[8],
                                          const bf16x8 (&dreg)[8], const u16 *bk, const u16 *bv,
-                                         const Seg &cs, int cj0, int bound, float lse2,
-                                         const f32x16 &ndelta, float c, int hf, const NatOff &no,
-                                         const TrOff &to) {
-  const bool need_mask = cj0 + kBN > cs.n_full;
+                                         bool need_mask, int lim, float lse2, const f32x16 &ndelta,
+                                         float c, const NatOff &no, const TrOff &to) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     // dP^T accumulates onto -Delta, so it comes out as dP - Delta
@@ -48,17 +49,16 @@ __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[
       s = mfma32(lds_nat_o(bk, 32 * kt, ks, no), qreg[ks], s);
       p = mfma32(lds_nat_o(bv, 32 * kt, ks, no), dreg[ks], p);
     }
+    if (need_mask) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int jj = 32 * kt + 8 * (v >> 2) + (v & 3);
+        s[v] = jj <= lim ? s[v] : kNegInf;
+      }
+    }
     float ds[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float pv = fast_exp2(fmaf(s[v], c, -lse2));
-      if (need_mask) {
-        const int jj = cj0 + 32 * kt + 8 * (v >> 2) + 4 * hf + (v & 3);
-        const bool vis = (jj < cs.n_hi) && (cs.cpos0 + jj <= bound);
-        pv = vis ? pv : 0.f;
-      }
-      ds[v] = pv * p[v];
-    }
+    for (int v = 0; v < 16; ++v) ds[v] = fast_exp2(fmaf(s[v], c, -lse2)) * p[v];
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       const bf16x8 db = pack8(ds + 8 * w);
@@ -149,7 +149,11 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
       const int cj0 = j0;
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
       if (sg < nseg) dma_kv(s, j0, sK1, sV1);
-      if (wave_active) dq_block(acc, qreg, dreg, sK0, sV0, cs, cj0, bound, lse2, ndelta, c, hf, no, to);
+      if (wave_active) {
+        const bool need = cj0 + kBN > cs.n_full;
+        const int lim = min(cs.n_hi - 1, bound - cs.cpos0) - cj0 - 4 * hf;
+        dq_block(acc, qreg, dreg, sK0, sV0, need, lim, lse2, ndelta, c, no, to);
+      }
       dma_wait();
       __syncthreads();
     }
@@ -159,7 +163,11 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
       const int cj0 = j0;
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
       if (sg < nseg) dma_kv(s, j0, sK0, sV0);
-      if (wave_active) dq_block(acc, qreg, dreg, sK1, sV1, cs, cj0, bound, lse2, ndelta, c, hf, no, to);
+      if (wave_active) {
+        const bool need = cj0 + kBN > cs.n_full;
+        const int lim = min(cs.n_hi - 1, bound - cs.cpos0) - cj0 - 4 * hf;
+        dq_block(acc, qreg, dreg, sK1, sV1, need, lim, lse2, ndelta, c, no, to);
+      }
       dma_wait();
       __syncthreads();
     }
