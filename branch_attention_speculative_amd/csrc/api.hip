@@ -283,7 +283,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     const float scale = resolve_scale(a->scale, p->d);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    float *delta = static_cast<float *>(a->workspace);
+    float *ndelta = static_cast<float *>(a->workspace);  // -Delta
     const size_t del_bytes = (size_t(p->n_local + p->n_branch) * p->hq * 4 + 255) & ~size_t(255);
     float *lse2 = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + del_bytes);
     float *dq_local = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + 2 * del_bytes);
@@ -296,7 +296,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     pa.lse = a->lse;
     pa.lseb = a->lseb;
     pa.bound_main = p->dev.bound_main;
-    pa.delta = delta;
+    pa.ndelta = ndelta;
     pa.lse2 = lse2;
     pa.n_local = int32_t(p->n_local);
     pa.n_branch = int32_t(p->n_branch);
@@ -312,7 +312,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
       b.vb = a->vb;
       b.doutb = a->doutb;
       b.lseb = a->lseb;
-      b.delta_b = delta + size_t(p->n_local) * p->hq;
+      b.ndelta_b = ndelta + size_t(p->n_local) * p->hq;
       b.dq_local = dq_local;
       b.dkb = a->dkb;
       b.dvb = a->dvb;
@@ -341,7 +341,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     q.doutb = a->doutb;
     q.lse = a->lse;
     q.lseb = a->lseb;
-    q.delta = delta;
+    q.ndelta = ndelta;
     q.lse2 = lse2;
     q.dq_local = dq_local;
     q.dq = a->dq;
@@ -370,7 +370,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     k.doutb = a->doutb;
     k.lse = a->lse;
     k.lseb = a->lseb;
-    k.delta = delta;
+    k.ndelta = ndelta;
     k.lse2 = lse2;
     k.dk = a->dk;
     k.dv = a->dv;

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
   if (pair < total && sub == 0) {
-    a.delta[pair] = pad ? 0.f : acc;
+    a.ndelta[pair] = pad ? 0.f : -acc;
     a.lse2[pair] = pad ? 0.f : l2;
   }
 }
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
         }
       }
       const float lse2 = a.lseb[qh] * kLog2e;
-      const float del = a.delta_b[qh];
+      const float ndel = a.ndelta_b[qh];
       for (int kl = 0; kl < t.rows; ++kl) {
         sP[tid * kMaxBranch + kl] = 0.f;
         sS[tid * kMaxBranch + kl] = 0.f;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
       for (int jj = 0; jj < MAXB; ++jj) {
         if (jj < nvis) {
           const float p = fast_exp2(s[jj] * a.scale_log2 - lse2);
-          const float d = p * (dp[jj] - del);
+          const float d = p * (dp[jj] + ndel);
           s[jj] = d;  // keep dS for the dQ sum
           sP[tid * kMaxBranch + kl0 + jj] = p;
           sS[tid * kMaxBranch + kl0 + jj] = d;

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
   const int64_t qh = int64_t(row) * a.hq + h;
   const int64_t qall = (t.src ? int64_t(a.n_local) * a.hq : 0) + qh;
   const float lse2 = (bound >= 0) ? a.lse2[qall] : 0.f;
-  const float delta = (bound >= 0) ? a.delta[qall] : 0.f;
+  const float ndel = (bound >= 0) ? a.ndelta[qall] : 0.f;
 
   bf16x8 qreg[8], dreg[8];
   {
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
   };
   f32x16 ndelta;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) ndelta[v] = -delta;
+  for (int v = 0; v < 16; ++v) ndelta[v] = ndel;
 
   lds_zero(sK0, kBN * kRS, tid, kDqWaves * 64);
   lds_zero(sV0, kBN * kRS, tid, kDqWaves * 64);
@@ -283,18 +283,18 @@ __device__ __forceinline__ void dv_phase2(f32x16 (&adv)[4], const bf16x8 (&pb)[4
 }
 
 // dK wave, phase 1: dP - Delta = dO V^T - Delta for 64 query vectors (the
-// product accumulates onto -Delta of each row).
+// product accumulates onto -Delta of each row, from LDS snd).
 __device__ __forceinline__ void dk_phase1(f32x16 (&dp)[2], const bf16x8 (&vreg)[8], const u16 *bd,
-                                          const float *sdel, int hf, const NatOff &no) {
+                                          const float *snd, int hf, const NatOff &no) {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     f32x16 p;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       // rows 32 mt + 8 g4 + 4 hf + 0..3 are four consecutive slots
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sdel + 32 * mt + 8 * g4 + 4 * hf);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(snd + 32 * mt + 8 * g4 + 4 * hf);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[4 * g4 + e] = -d4[e];
+      for (int e = 0; e < 4; ++e) p[4 * g4 + e] = d4[e];
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) p = mfma32(lds_nat_o(bd, 32 * mt, ks, no), vreg[ks], p);
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     const int rr = min(qb.r0 + (lane >> log2G), qb.hi - 1);
     const int64_t qh = base + int64_t(rr) * hq + hb + (lane & (G - 1));
     if (wave == 1) dma_dword64(dl, a.lse2 + qh);
-    if (wave == 2) dma_dword64(de, a.delta + qh);
+    if (wave == 2) dma_dword64(de, a.ndelta + qh);
     if (wave == 3) dma_dword64(db, (qb.src ? a.bound_branch : a.bound_main) + rr);
   };
   // no mask when every row of the block sees every key of the tile; rows

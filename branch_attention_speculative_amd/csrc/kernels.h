@@ -37,12 +37,13 @@ struct FwdBranchArgs {
   float scale_log2;
 };
 
-// Delta = rowsum(dO * O) for main rows then branch rows.
+// -Delta = -rowsum(dO * O) for main rows then branch rows (stored negated:
+// the kernels that use it accumulate dP onto it).
 struct BwdPreArgs {
   const void *o, *ob, *dout, *doutb;
   const float *lse, *lseb;
   const int32_t *bound_main;
-  float *delta;  // [(N + NB) * hq]
+  float *ndelta;  // [(N + NB) * hq]
   float *lse2;   // [(N + NB) * hq]: LSE * log2(e)
   int32_t n_local, n_branch, hq, d;
 };
@@ -50,7 +51,7 @@ struct BwdPreArgs {
 // Branch-local backward: the branch-key share of dQ (to workspace), dKb, dVb.
 struct BwdBranchArgs {
   const void *qb, *kb, *vb, *doutb;
-  const float *lseb, *delta_b;
+  const float *lseb, *ndelta_b;  // ndelta_b: -Delta of the branch rows
   float *dq_local;  // [NB, hq, d] fp32
   void *dkb, *dvb;
   const BTile *btiles;
@@ -62,7 +63,7 @@ struct BwdBranchArgs {
 // Ring replay for dQ (query-stationary).
 struct BwdDqArgs {
   const void *q, *qb, *k, *v, *dout, *doutb;
-  const float *lse, *lseb, *delta;  // delta: main rows then branch rows
+  const float *lse, *lseb, *ndelta;  // -Delta: main rows then branch rows
   const float *lse2;                // LSE * log2(e), main rows then branch rows
   const float *dq_local;            // branch rows: branch-key share of dQ
   void *dq, *dqb;
@@ -75,7 +76,7 @@ struct BwdDqArgs {
 // Ring replay for dK/dV (key-stationary).
 struct BwdDkdvArgs {
   const void *q, *qb, *k, *v, *dout, *doutb;
-  const float *lse, *lseb, *delta, *lse2;
+  const float *lse, *lseb, *ndelta, *lse2;  // ndelta: -Delta
   void *dk, *dv;
   const KTile *ktiles;
   const int32_t *bound_main, *bound_branch;

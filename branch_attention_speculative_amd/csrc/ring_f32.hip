@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdDqArgs a, F32Shape s
   for (int d = 0; d < DIM; ++d) dq[d] = 0.f;
   if (bound >= 0) {
     const float lse2 = (main ? a.lse[qh] : a.lseb[qh]) * kLog2e;
-    const float del = a.delta[gid];
+    const float ndel = a.ndelta[gid];
     const int c = sh.chunk[s], off = sh.cu_local[s];
     for (int i = 0; i < sh.C; ++i) {
       int shard = sh.r - i;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdDqArgs a, F32Shape s
             dp = fmaf(DO[qh * DIM + d], V[ko + d], dp);
           }
           const float p = exp2f(x * sh.scale_log2 - lse2);
-          const float ds = p * (dp - del);
+          const float ds = p * (dp + ndel);
 #pragma unroll
           for (int d = 0; d < DIM; ++d) dq[d] = fmaf(ds, K[ko + d], dq[d]);
         }
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdDkdvArgs a, F32Sha
       const float *DO = static_cast<const float *>(src ? a.doutb : a.dout);
       const float *LSE = src ? a.lseb : a.lse;
       const int32_t *BOUND = src ? sh.bound_branch : sh.bound_main;
-      const float *DEL = a.delta + (src ? int64_t(sh.n_local) * sh.hq : 0);
+      const float *NDEL = a.ndelta + (src ? int64_t(sh.n_local) * sh.hq : 0);
       const int lo = src ? sh.branch_off[sh.seq_a0[s]] : sh.cu_local[s];
       const int hi = src ? sh.branch_off[sh.seq_a0[s + 1]] : sh.cu_local[s + 1];
       for (int q = lo; q < hi; ++q) {
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdDkdvArgs a, F32Sha
             dp = fmaf(DO[qh * DIM + d], V[ko + d], dp);
           }
           const float p = exp2f(x * sh.scale_log2 - LSE[qh] * kLog2e);
-          const float ds = p * (dp - DEL[qh]);
+          const float ds = p * (dp + NDEL[qh]);
 #pragma unroll
           for (int d = 0; d < DIM; ++d) {
             dk[d] = fmaf(ds, Q[qh * DIM + d], dk[d]);
