@@ -33,7 +33,7 @@ def env():
     return torch, ba
 
 
-def _run(env, w, with_bwd, oracle_dtype=np.float32):
+def _run(env, w, with_bwd, oracle_dtype=np.float32, prep=None):
     torch, ba = env
     say(f"[case] {w.name}: lens={w.seqlens[:6]}{'...' if len(w.seqlens) > 6 else ''} C={w.C} r={w.r} "
         f"kind={w.kind} depth/block={w.depth_or_block} heads={w.hq}/{w.hkv} d={w.d} {w.dtype}")
@@ -42,6 +42,9 @@ def _run(env, w, with_bwd, oracle_dtype=np.float32):
     N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
     assert (N, NB) == (lay["n_local"], br["n_branch"])
     raw, dec = inputs(w, N, NB)
+    if prep is not None:  # reshape the inputs; both sides then see the same values
+        prep(w, lay, raw)
+        dec = {k: workloads.as_f32(w, v) for k, v in raw.items()}
     dev = {k: to_device(torch, w, v) for k, v in raw.items()}
     o, lse, ob, lseb = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
     res = dict(o=o, lse=lse, ob=ob, lseb=lseb)
@@ -157,6 +160,37 @@ def test_edge_cases(env, w):
     got, ref, _ = _run(env, w, with_bwd=True)
     _check_fwd(w, got, ref)
     _check_bwd(w, got, ref)
+
+
+def _shift_late_keys(lam):
+    """Add lam * u (u a fixed unit vector) to every main key in the second
+    half of its sequence. A query's scores against those keys move by
+    lam * scale * <q, u> together: for queries with <q, u> > 0 they jump far
+    above the running max taken from earlier key blocks (the overflow redo of
+    the lazy max), for <q, u> < 0 they fall far below it (underflow). Inside
+    each half the attention stays as diffuse as with plain N(0, 1) data."""
+    def prep(w, lay, raw):
+        k = workloads.as_f32(w, raw["k"]).copy()
+        u = np.random.default_rng(99).standard_normal(w.d).astype(np.float32)
+        u /= np.linalg.norm(u)
+        for s_ in range(w.C):
+            ls = pack.zigzag_layout(w.seqlens, w.C, s_)
+            late = ls["pos"] >= (ls["L"][ls["seq"]] + 1) // 2
+            k[s_][late] += lam * u
+        raw["k"] = workloads.f32_to_bf16_bits(k) if w.dtype == "bf16" else k
+    return prep
+
+
+def test_running_max_far_from_first_block(env):
+    """Scores jumping about +-100 (log2 units) away from the first key block's:
+    exercises the overflow redo of the forward's lazy running max and the
+    underflow of blocks far below it. Forward only: the backward uses the
+    final LSE and has no running max, and with a key component this large dQ
+    is dominated by the cancellation of sum_k dS (which is zero per row) times
+    that component, below what bf16 dS can resolve in any implementation."""
+    w = _edge("maxjump", [1999, 700], 2, 1, pack.KIND_TTT, 2, 8, 2)
+    got, ref, _ = _run(env, w, with_bwd=False, prep=_shift_late_keys(600.0))
+    _check_fwd(w, got, ref)
 
 
 def test_forward_is_deterministic_and_stream_ordered(env):
