@@ -371,25 +371,30 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   const NatOff no = nat_offsets(lane);
   const TrOff to = tr_offsets(lane);
   // tile row mq is query vector (row r0 + mq / G, head g G + mq % G)
-  const DmaOff<8> dof = dma_offsets<8>(
-      wave, lane, [&](int mq) { return (int64_t(mq >> log2G) * hq + (mq & (G - 1))) * 128; });
-  // issue the loads of inner block b into one buffer set
+  const DmaOff<4> dof = dma_offsets<4>(
+      wave & 3, lane, [&](int mq) { return (int64_t(mq >> log2G) * hq + (mq & (G - 1))) * 128; });
+  // Issue the loads of inner block b into one buffer set. Only the four dV
+  // waves (0-3) load: the per-row data first (waves 1-3), then the Q / dO
+  // tiles (all four). The dK waves, one block behind, issue no loads; this
+  // measured about 4% faster than all eight waves sharing the tile loads.
   auto dma_block = [&](int b, u16 *dq, u16 *dd, float *dl, float *de, int *db) {
     const QBlock qb = qblock(t, b, RB, nb_main);
-    const u16 *Q = static_cast<const u16 *>(qb.src ? a.qb : a.q);
-    const u16 *DO = static_cast<const u16 *>(qb.src ? a.doutb : a.dout);
     const int hb = t.g * G;
-    // query vectors past the range are not read (their P is masked to zero)
-    const int64_t off = (int64_t(qb.r0) * hq + hb) * 128;
-    const uint32_t bytes = uint32_t(((int64_t(qb.nr - 1) * hq + G - 1) * 128 + 128) * 2);
-    dma_tile64_buf<8>(dq, buf_rsrc(Q + off, bytes), dof, wave);
-    dma_tile64_buf<8>(dd, buf_rsrc(DO + off, bytes), dof, wave);
     const int64_t base = qb.src ? int64_t(a.n_local) * hq : 0;
     const int rr = min(qb.r0 + (lane >> log2G), qb.hi - 1);
     const int64_t qh = base + int64_t(rr) * hq + hb + (lane & (G - 1));
     if (wave == 1) dma_dword64(dl, a.lse2 + qh);
     if (wave == 2) dma_dword64(de, a.ndelta + qh);
     if (wave == 3) dma_dword64(db, (qb.src ? a.bound_branch : a.bound_main) + rr);
+    if (wave < 4) {
+      const u16 *Q = static_cast<const u16 *>(qb.src ? a.qb : a.q);
+      const u16 *DO = static_cast<const u16 *>(qb.src ? a.doutb : a.dout);
+      // query vectors past the range are not read (their P is masked to zero)
+      const int64_t off = (int64_t(qb.r0) * hq + hb) * 128;
+      const uint32_t bytes = uint32_t(((int64_t(qb.nr - 1) * hq + G - 1) * 128 + 128) * 2);
+      dma_tile64_buf<4>(dq, buf_rsrc(Q + off, bytes), dof, wave);
+      dma_tile64_buf<4>(dd, buf_rsrc(DO + off, bytes), dof, wave);
+    }
   };
   // no mask when every row of the block sees every key of the tile; rows
   // are in increasing bound order, so the first row's bound (sb[0], the
@@ -418,9 +423,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   lds_zero(sD2, kQB * kRS, tid, 512);
   __syncthreads();
 
-  // Iteration b = 0 .. nb: one barrier, the loads of block b + 1, then the
-  // dV waves do block b (S, P -> exchange slot b % 3, dV) and the dK waves
-  // do block b - 1 (dP, dS with P from slot (b - 1) % 3, dK). The barrier at
+  // Iteration b = 0 .. nb: one barrier, then the dV waves issue the loads of
+  // block b + 1 and do block b (S, P -> exchange slot b % 3, dV) while the
+  // dK waves do block b - 1 (dP, dS with P from slot (b - 1) % 3, dK). The barrier at
   // the top of iteration b publishes block b's tiles and P of block b - 1,
   // and frees the set and slot that iteration b + 1 overwrites.
   if (nb > 0) dma_block(0, sQ0, sD0, sL0, sE0, sB0);
@@ -452,25 +457,22 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
       iter(b + 2, sQ2, sD2, sL2, sB2, sX2, sQ0, sD0, sL0, sE0, sB0);
     }
   } else {
-    // block b - 1 in the set (Qp, Dp, Ep); block b + 1 loads into the next set
-    auto iter = [&](int b, const u16 *Qp, const u16 *Dp, const float *Ep, const uint32_t *Xp,
-                    u16 *Qn, u16 *Dn, float *Ln, float *En, int *Bn) {
+    // block b - 1 in the set (Qp, Dp, Ep)
+    auto iter = [&](int b, const u16 *Qp, const u16 *Dp, const float *Ep, const uint32_t *Xp) {
       __syncthreads();
-      if (b + 1 < nb) dma_block(b + 1, Qn, Dn, Ln, En, Bn);
       if (wave_active && b >= 1) {
         const uint32_t *xs = Xp + xo;  // P of block b - 1
         f32x16 dp[2];
         dk_phase1(dp, kvreg, Dp, Ep, hf, no);
         dk_phase2(acc, dp, Qp, xs, lane, to);
       }
-      dma_wait();
     };
     for (int b = 0; b <= nb; b += 3) {
-      iter(b, sQ2, sD2, sE2, sX2, sQ1, sD1, sL1, sE1, sB1);
+      iter(b, sQ2, sD2, sE2, sX2);
       if (b + 1 > nb) break;
-      iter(b + 1, sQ0, sD0, sE0, sX0, sQ2, sD2, sL2, sE2, sB2);
+      iter(b + 1, sQ0, sD0, sE0, sX0);
       if (b + 2 > nb) break;
-      iter(b + 2, sQ1, sD1, sE1, sX1, sQ0, sD0, sL0, sE0, sB0);
+      iter(b + 2, sQ1, sD1, sE1, sX1);
     }
   }
 
