@@ -56,6 +56,24 @@ __device__ __forceinline__ void ld8<float>(const float *p, int64_t i, float (&o)
   }
 }
 
+// load 4 consecutive elements as floats (8-byte aligned for bf16, 16 for fp32)
+template <typename T>
+__device__ __forceinline__ void ld4(const T *p, int64_t i, float (&o)[4]);
+template <>
+__device__ __forceinline__ void ld4<u16>(const u16 *p, int64_t i, float (&o)[4]) {
+  const u32x2 x = *reinterpret_cast<const u32x2 *>(p + i);
+  o[0] = __uint_as_float(x.x << 16);
+  o[1] = __uint_as_float(x.x & 0xffff0000u);
+  o[2] = __uint_as_float(x.y << 16);
+  o[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void ld4<float>(const float *p, int64_t i, float (&o)[4]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p + i);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = a[k];
+}
+
 template <typename T>
 __device__ __forceinline__ void st8(T *p, int64_t i, const float (&v)[8]);
 template <>
@@ -72,21 +90,17 @@ __device__ __forceinline__ void st8<float>(float *p, int64_t i, const float (&v)
 }
 
 // Stage the branch keys/values of a tile (rows [base, base + rows), kv-head g)
-// in LDS as floats, row-major [row][DIM].
+// in LDS in the input type, row-major [row][DIM] (half the LDS of floats for
+// bf16, so that more workgroups fit on a compute unit).
 template <typename T, int DIM>
 __device__ __forceinline__ void stage_branch_kv(const T *KB, const T *VB, int base, int rows,
-                                                int g, int hkv, float *sK, float *sV) {
-  for (int id = threadIdx.x; id < rows * (DIM / 8); id += blockDim.x) {
-    const int rr = id / (DIM / 8), dc = id % (DIM / 8);
-    const int64_t off = (int64_t(base + rr) * hkv + g) * DIM + dc * 8;
-    float k8[8], v8[8];
-    ld8<T>(KB, off, k8);
-    ld8<T>(VB, off, v8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sK[rr * DIM + dc * 8 + e] = k8[e];
-      sV[rr * DIM + dc * 8 + e] = v8[e];
-    }
+                                                int g, int hkv, T *sK, T *sV) {
+  constexpr int PER = 16 / sizeof(T);  // elements per 16-byte chunk
+  for (int id = threadIdx.x; id < rows * (DIM / PER); id += blockDim.x) {
+    const int rr = id / (DIM / PER), dc = id % (DIM / PER);
+    const int64_t off = (int64_t(base + rr) * hkv + g) * DIM + dc * PER;
+    *reinterpret_cast<u32x4 *>(sK + rr * DIM + dc * PER) = *reinterpret_cast<const u32x4 *>(KB + off);
+    *reinterpret_cast<u32x4 *>(sV + rr * DIM + dc * PER) = *reinterpret_cast<const u32x4 *>(VB + off);
   }
 }
 
@@ -94,8 +108,8 @@ __device__ __forceinline__ void stage_branch_kv(const T *KB, const T *VB, int ba
 
 template <typename T, int DIM, int MAXB>
 __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
-  __shared__ float sK[kMaxBranch * DIM];
-  __shared__ float sV[kMaxBranch * DIM];
+  __shared__ __attribute__((aligned(16))) T sK[kMaxBranch * DIM];
+  __shared__ __attribute__((aligned(16))) T sV[kMaxBranch * DIM];
   const BTile t = a.btiles[blockIdx.x];
   if (t.rows == 0) return;
   const int base = a.branch_off[t.a0];
@@ -123,7 +137,8 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) {
         if (jj < nvis) {
-          const float *kr = sK + (kl0 + jj) * DIM + dc * 8;
+          float kr[8];
+          ld8<T>(sK, (kl0 + jj) * DIM + dc * 8, kr);
           float acc = s[jj];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc = fmaf(q8[e], kr[e], acc);
@@ -162,7 +177,8 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) {
         if (jj < nvis) {
-          const float *vr = sV + (kl0 + jj) * DIM + dc * 8;
+          float vr[8];
+          ld8<T>(sV, (kl0 + jj) * DIM + dc * 8, vr);
 #pragma unroll
           for (int e = 0; e < 8; ++e) o8[e] = fmaf(s[jj], vr[e], o8[e]);
         }
@@ -219,10 +235,12 @@ constexpr int kBQ = 128;  // query vectors per backward chunk
 
 template <typename T, int DIM, int MAXB>
 __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
-  __shared__ float sK[kMaxBranch * DIM];
-  __shared__ float sV[kMaxBranch * DIM];
-  __shared__ float sP[kBQ * kMaxBranch];
-  __shared__ float sS[kBQ * kMaxBranch];
+  // K / V in the input type; P and dS of each query vector of a chunk against
+  // the keys of its own anchor (index 0 = the anchor's first key)
+  __shared__ __attribute__((aligned(16))) T sK[kMaxBranch * DIM];
+  __shared__ __attribute__((aligned(16))) T sV[kMaxBranch * DIM];
+  __shared__ float sP[kBQ * MAXB];
+  __shared__ float sS[kBQ * MAXB];
   const BTile t = a.btiles[blockIdx.x];
   if (t.rows == 0) return;
   const int base = a.branch_off[t.a0];
@@ -264,8 +282,9 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
 #pragma unroll
         for (int jj = 0; jj < MAXB; ++jj) {
           if (jj < nvis) {
-            const float *kr = sK + (kl0 + jj) * DIM + dc * 8;
-            const float *vr = sV + (kl0 + jj) * DIM + dc * 8;
+            float kr[8], vr[8];
+            ld8<T>(sK, (kl0 + jj) * DIM + dc * 8, kr);
+            ld8<T>(sV, (kl0 + jj) * DIM + dc * 8, vr);
             float as = s[jj], ad = dp[jj];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -279,20 +298,18 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
       }
       const float lse2 = a.lseb[qh] * kLog2e;
       const float ndel = a.ndelta_b[qh];
-      for (int kl = 0; kl < t.rows; ++kl) {
-        sP[tid * kMaxBranch + kl] = 0.f;
-        sS[tid * kMaxBranch + kl] = 0.f;
-      }
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) {
         if (jj < nvis) {
           const float p = fast_exp2(s[jj] * a.scale_log2 - lse2);
           const float d = p * (dp[jj] + ndel);
           s[jj] = d;  // keep dS for the dQ sum
-          sP[tid * kMaxBranch + kl0 + jj] = p;
-          sS[tid * kMaxBranch + kl0 + jj] = d;
+          sP[tid * MAXB + jj] = p;
+          sS[tid * MAXB + jj] = d;
         } else {
           s[jj] = 0.f;
+          sP[tid * MAXB + jj] = 0.f;
+          sS[tid * MAXB + jj] = 0.f;
         }
       }
       for (int dc = 0; dc < DIM / 8; ++dc) {
@@ -302,7 +319,8 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
 #pragma unroll
         for (int jj = 0; jj < MAXB; ++jj) {
           if (jj < nvis) {
-            const float *kr = sK + (kl0 + jj) * DIM + dc * 8;
+            float kr[8];
+            ld8<T>(sK, (kl0 + jj) * DIM + dc * 8, kr);
 #pragma unroll
             for (int e = 0; e < 8; ++e) o8[e] = fmaf(s[jj], kr[e], o8[e]);
           }
@@ -323,17 +341,21 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
         const int lo = a.branch_off[an] - base;
         const int hi = a.branch_off[an + 1] - base;
         const int q_lo = max(lo * G, c0), q_hi = min(hi * G, c0 + nq);
+        // this key is entry kl - lo of its anchor's queries' P / dS rows
         for (int qv = q_lo; qv < q_hi; ++qv) {
-          const float p = sP[(qv - c0) * kMaxBranch + kl];
-          const float d = sS[(qv - c0) * kMaxBranch + kl];
+          const float p = sP[(qv - c0) * MAXB + kl - lo];
+          const float d = sS[(qv - c0) * MAXB + kl - lo];
           if (p == 0.f && d == 0.f) continue;
           const int row = base + qv / G;
           const int h = t.g * G + qv % G;
           const int64_t off = (int64_t(row) * a.hq + h) * DIM + d4 * 4;
+          float q4[4], o4[4];
+          ld4<T>(QB, off, q4);
+          ld4<T>(DOB, off, o4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            adk[it][e] = fmaf(d, ldf<T>(QB, off + e), adk[it][e]);
-            adv[it][e] = fmaf(p, ldf<T>(DOB, off + e), adv[it][e]);
+            adk[it][e] = fmaf(d, q4[e], adk[it][e]);
+            adv[it][e] = fmaf(p, o4[e], adv[it][e]);
           }
         }
       }
