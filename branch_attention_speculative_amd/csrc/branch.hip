@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
 
 // ---------------------------------------------------------------------------
 
-constexpr int kBQ = 128;  // query vectors per backward chunk
+constexpr int kBQ = 64;  // query vectors per backward chunk (four threads each)
 
 template <typename T, int DIM, int MAXB>
 __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
@@ -258,11 +258,14 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) adk[it][e] = adv[it][e] = 0.f;
   const int nqv = t.rows * G;
+  // phase 1: four threads per query vector of the chunk, each over a quarter of D
+  const int ql = tid >> 2, sub = tid & 3;
+  constexpr int QD = DIM / 4;  // dims per thread
   for (int c0 = 0; c0 < nqv; c0 += kBQ) {
     const int nq = min(kBQ, nqv - c0);
     __syncthreads();  // staged K/V visible; previous chunk's sP/sS reads done
-    if (tid < nq) {
-      const int qv = c0 + tid;
+    if (ql < nq) {  // uniform over each group of four
+      const int qv = c0 + ql;
       const int row = base + qv / G;
       const int h = t.g * G + qv % G;
       const int an = a.b_anchor[row];
@@ -275,16 +278,18 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
       float s[MAXB], dp[MAXB];
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) s[jj] = dp[jj] = 0.f;
-      for (int dc = 0; dc < DIM / 8; ++dc) {
+#pragma unroll
+      for (int dc = 0; dc < QD / 8; ++dc) {
+        const int d0 = sub * QD + dc * 8;
         float q8[8], d8[8];
-        ld8<T>(QB, qh * DIM + dc * 8, q8);
-        ld8<T>(DOB, qh * DIM + dc * 8, d8);
+        ld8<T>(QB, qh * DIM + d0, q8);
+        ld8<T>(DOB, qh * DIM + d0, d8);
 #pragma unroll
         for (int jj = 0; jj < MAXB; ++jj) {
           if (jj < nvis) {
             float kr[8], vr[8];
-            ld8<T>(sK, (kl0 + jj) * DIM + dc * 8, kr);
-            ld8<T>(sV, (kl0 + jj) * DIM + dc * 8, vr);
+            ld8<T>(sK, (kl0 + jj) * DIM + d0, kr);
+            ld8<T>(sV, (kl0 + jj) * DIM + d0, vr);
             float as = s[jj], ad = dp[jj];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -296,23 +301,33 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
           }
         }
       }
+      // full dot products: sum over the four quarters
+#pragma unroll
+      for (int jj = 0; jj < MAXB; ++jj) {
+        s[jj] += __shfl_xor(s[jj], 1, 4);
+        s[jj] += __shfl_xor(s[jj], 2, 4);
+        dp[jj] += __shfl_xor(dp[jj], 1, 4);
+        dp[jj] += __shfl_xor(dp[jj], 2, 4);
+      }
       const float lse2 = a.lseb[qh] * kLog2e;
       const float ndel = a.ndelta_b[qh];
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) {
+        float p = 0.f, d = 0.f;
         if (jj < nvis) {
-          const float p = fast_exp2(s[jj] * a.scale_log2 - lse2);
-          const float d = p * (dp[jj] + ndel);
-          s[jj] = d;  // keep dS for the dQ sum
-          sP[tid * MAXB + jj] = p;
-          sS[tid * MAXB + jj] = d;
-        } else {
-          s[jj] = 0.f;
-          sP[tid * MAXB + jj] = 0.f;
-          sS[tid * MAXB + jj] = 0.f;
+          p = fast_exp2(s[jj] * a.scale_log2 - lse2);
+          d = p * (dp[jj] + ndel);
+        }
+        s[jj] = d;  // keep dS for the dQ sum
+        if (sub == 0) {
+          sP[ql * MAXB + jj] = p;
+          sS[ql * MAXB + jj] = d;
         }
       }
-      for (int dc = 0; dc < DIM / 8; ++dc) {
+      // this thread's quarter of the branch-key share of dQ
+#pragma unroll
+      for (int dc = 0; dc < QD / 8; ++dc) {
+        const int d0 = sub * QD + dc * 8;
         float o8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o8[e] = 0.f;
@@ -320,14 +335,14 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
         for (int jj = 0; jj < MAXB; ++jj) {
           if (jj < nvis) {
             float kr[8];
-            ld8<T>(sK, (kl0 + jj) * DIM + dc * 8, kr);
+            ld8<T>(sK, (kl0 + jj) * DIM + d0, kr);
 #pragma unroll
             for (int e = 0; e < 8; ++e) o8[e] = fmaf(s[jj], kr[e], o8[e]);
           }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) o8[e] *= a.scale;
-        st8<float>(a.dq_local, qh * DIM + dc * 8, o8);
+        st8<float>(a.dq_local, qh * DIM + d0, o8);
       }
     }
     __syncthreads();
