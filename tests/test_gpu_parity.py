@@ -148,6 +148,10 @@ EDGES = [
     _edge("g16", [257, 100], 4, 2, pack.KIND_BLOCK_CAUSAL, 0, 16, 1,
           anchors=[3, 100, 256, 300], blens=[8, 16, 8, 16]),
     _edge("g64", [129], 2, 0, pack.KIND_TTT, 1, 64, 1),
+    # causal blocks of up to 32 keys (the 32-key instance of the branch kernels),
+    # all anchors inside rank 1's chunks of both sequences
+    _edge("block-32", [300, 90], 2, 1, pack.KIND_BLOCK_CAUSAL, 0, 8, 1,
+          anchors=[80, 150, 220, 330, 360], blens=[32, 17, 25, 32, 9]),
     # block kind with no anchors at all on this rank
     _edge("block-empty", [64, 64], 4, 3, pack.KIND_BLOCK_BIDIR, 16, 8, 2, anchors=[0], blens=[4]),
     # a long single chunk: several key blocks per shard, ragged tails
