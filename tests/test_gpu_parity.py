@@ -148,6 +148,9 @@ EDGES = [
     _edge("g16", [257, 100], 4, 2, pack.KIND_BLOCK_CAUSAL, 0, 16, 1,
           anchors=[3, 100, 256, 300], blens=[8, 16, 8, 16]),
     _edge("g64", [129], 2, 0, pack.KIND_TTT, 1, 64, 1),
+    _edge("g2", [333], 2, 1, pack.KIND_TTT, 2, 4, 2),
+    _edge("g8", [150, 77], 4, 3, pack.KIND_BLOCK_BIDIR, 0, 16, 2,
+          anchors=[60, 80, 185, 195], blens=[6, 12, 3, 16]),
     # causal blocks of up to 32 keys (the 32-key instance of the branch kernels),
     # all anchors inside rank 1's chunks of both sequences
     _edge("block-32", [300, 90], 2, 1, pack.KIND_BLOCK_CAUSAL, 0, 8, 1,
