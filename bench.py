@@ -258,6 +258,16 @@ def main():
         "kernels": kernels,
         "wall_s": wall,
     }
+    if kernels:
+        # forward and backward separately, from the per-kernel event times
+        fwd_ms = sum(k["avg_ms"] * k["launches_per_step"] for n, k in kernels.items()
+                     if n.startswith("fwd"))
+        bwd_ms = sum(k["avg_ms"] * k["launches_per_step"] for n, k in kernels.items()
+                     if n.startswith("bwd"))
+        f_fwd, f_bwd = pairs * w.hq * w.d * 4, pairs * w.hq * w.d * 10
+        out["split"] = {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+                        "fwd_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,
+                        "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12 if bwd_ms else None}
     print(json.dumps(out))
 
 
