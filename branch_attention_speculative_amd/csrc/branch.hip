@@ -118,7 +118,11 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
   stage_branch_kv<T, DIM>(static_cast<const T *>(a.kb), static_cast<const T *>(a.vb), base, t.rows,
                           t.g, a.hkv, sK, sV);
   __syncthreads();
-  for (int qv = threadIdx.x; qv < t.rows * G; qv += blockDim.x) {
+  // four threads per query vector, each over a quarter of D: contiguous
+  // reads of q and of the partial, contiguous writes of the output
+  const int ql = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  constexpr int QD = DIM / 4;
+  for (int qv = ql; qv < t.rows * G; qv += blockDim.x / 4) {  // uniform per group of four
     const int row = base + qv / G;
     const int h = t.g * G + qv % G;
     const int an = a.b_anchor[row];
@@ -131,20 +135,28 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
     float s[MAXB];
 #pragma unroll
     for (int jj = 0; jj < MAXB; ++jj) s[jj] = 0.f;
-    for (int dc = 0; dc < DIM / 8; ++dc) {
+#pragma unroll
+    for (int dc = 0; dc < QD / 8; ++dc) {
+      const int d0 = sub * QD + dc * 8;
       float q8[8];
-      ld8<T>(QB, qh * DIM + dc * 8, q8);
+      ld8<T>(QB, qh * DIM + d0, q8);
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) {
         if (jj < nvis) {
           float kr[8];
-          ld8<T>(sK, (kl0 + jj) * DIM + dc * 8, kr);
+          ld8<T>(sK, (kl0 + jj) * DIM + d0, kr);
           float acc = s[jj];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc = fmaf(q8[e], kr[e], acc);
           s[jj] = acc;
         }
       }
+    }
+    // full dot products: sum over the four quarters
+#pragma unroll
+    for (int jj = 0; jj < MAXB; ++jj) {
+      s[jj] += __shfl_xor(s[jj], 1, 4);
+      s[jj] += __shfl_xor(s[jj], 2, 4);
     }
     // branch partial: max and sum in the log2 domain
     float mb = kNegInf;
@@ -170,7 +182,9 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
     const float norm = 1.f / (wm + wb);
     const float cm = wm * norm, cb = wb * norm / lsum;
     T *OB = static_cast<T *>(a.ob);
-    for (int dc = 0; dc < DIM / 8; ++dc) {
+#pragma unroll
+    for (int dc = 0; dc < QD / 8; ++dc) {
+      const int d0 = sub * QD + dc * 8;
       float o8[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o8[e] = 0.f;
@@ -178,18 +192,18 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
       for (int jj = 0; jj < MAXB; ++jj) {
         if (jj < nvis) {
           float vr[8];
-          ld8<T>(sV, (kl0 + jj) * DIM + dc * 8, vr);
+          ld8<T>(sV, (kl0 + jj) * DIM + d0, vr);
 #pragma unroll
           for (int e = 0; e < 8; ++e) o8[e] = fmaf(s[jj], vr[e], o8[e]);
         }
       }
       float m8[8];
-      ld8<float>(a.om, qh * DIM + dc * 8, m8);
+      ld8<float>(a.om, qh * DIM + d0, m8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o8[e] = cm * m8[e] + cb * o8[e];
-      st8<T>(OB, qh * DIM + dc * 8, o8);
+      st8<T>(OB, qh * DIM + d0, o8);
     }
-    a.lseb[qh] = l2 * kLn2;
+    if (sub == 0) a.lseb[qh] = l2 * kLn2;
   }
 }
 
