@@ -56,6 +56,32 @@ __device__ __forceinline__ void ld8<float>(const float *p, int64_t i, float (&o)
   }
 }
 
+// load 8 consecutive elements as floats and keep a raw copy of them in LDS
+template <typename T>
+__device__ __forceinline__ void ld8_keep(const T *p, int64_t i, T *lds, float (&o)[8]);
+template <>
+__device__ __forceinline__ void ld8_keep<u16>(const u16 *p, int64_t i, u16 *lds, float (&o)[8]) {
+  const u32x4 x = *reinterpret_cast<const u32x4 *>(p + i);
+  *reinterpret_cast<u32x4 *>(lds) = x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(x[k] << 16);
+    o[2 * k + 1] = __uint_as_float(x[k] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void ld8_keep<float>(const float *p, int64_t i, float *lds, float (&o)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p + i);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + i + 4);
+  *reinterpret_cast<f32x4 *>(lds) = a;
+  *reinterpret_cast<f32x4 *>(lds + 4) = b;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = a[k];
+    o[4 + k] = b[k];
+  }
+}
+
 // load 4 consecutive elements as floats (8-byte aligned for bf16, 16 for fp32)
 template <typename T>
 __device__ __forceinline__ void ld4(const T *p, int64_t i, float (&o)[4]);
@@ -255,6 +281,9 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
   __shared__ __attribute__((aligned(16))) T sV[kMaxBranch * DIM];
   __shared__ float sP[kBQ * MAXB];
   __shared__ float sS[kBQ * MAXB];
+  // q and dO of the chunk's query vectors, kept from phase 1 for phase 2
+  __shared__ __attribute__((aligned(16))) T sQ[kBQ * DIM];
+  __shared__ __attribute__((aligned(16))) T sDO[kBQ * DIM];
   const BTile t = a.btiles[blockIdx.x];
   if (t.rows == 0) return;
   const int base = a.branch_off[t.a0];
@@ -296,8 +325,8 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
       for (int dc = 0; dc < QD / 8; ++dc) {
         const int d0 = sub * QD + dc * 8;
         float q8[8], d8[8];
-        ld8<T>(QB, qh * DIM + d0, q8);
-        ld8<T>(DOB, qh * DIM + d0, d8);
+        ld8_keep<T>(QB, qh * DIM + d0, sQ + ql * DIM + d0, q8);
+        ld8_keep<T>(DOB, qh * DIM + d0, sDO + ql * DIM + d0, d8);
 #pragma unroll
         for (int jj = 0; jj < MAXB; ++jj) {
           if (jj < nvis) {
@@ -375,12 +404,9 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
           const float p = sP[(qv - c0) * MAXB + kl - lo];
           const float d = sS[(qv - c0) * MAXB + kl - lo];
           if (p == 0.f && d == 0.f) continue;
-          const int row = base + qv / G;
-          const int h = t.g * G + qv % G;
-          const int64_t off = (int64_t(row) * a.hq + h) * DIM + d4 * 4;
           float q4[4], o4[4];
-          ld4<T>(QB, off, q4);
-          ld4<T>(DOB, off, o4);
+          ld4<T>(sQ, (qv - c0) * DIM + d4 * 4, q4);
+          ld4<T>(sDO, (qv - c0) * DIM + d4 * 4, o4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             adk[it][e] = fmaf(d, q4[e], adk[it][e]);
