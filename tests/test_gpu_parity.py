@@ -216,6 +216,52 @@ def test_forward_is_deterministic_and_stream_ordered(env):
         assert torch.equal(x, y)
 
 
+def test_graph_capture_replays_match_eager(env):
+    # fwd + bwd enqueue kernels only (no allocation, memset or sync inside),
+    # so one step can be captured in a HIP graph. Every replay, with new input
+    # values written in place and an eager step plus syncs before it, must
+    # equal the eager result bit for bit.
+    torch, ba = env
+    w = workloads.make("dflash_r")
+    say(f"[case] graph capture, {w.name}")
+    plan = make_plan(ba, w)
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    names = ["q", "k", "v", "qb", "kb", "vb", "do", "dob"]
+    raw, _ = inputs(w, N, NB, names=names)
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    wsf = torch.empty(max(plan.info["ws_fwd_bytes"], 1), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(plan.info["ws_bwd_bytes"], 1), dtype=torch.uint8, device="cuda")
+    out_names = ("o", "lse", "ob", "lseb", "dq", "dk", "dv", "dqb", "dkb", "dvb")
+
+    def step():
+        ins = [dev[k] for k in names[:6]]
+        o, lse, ob, lseb = ba.fwd(plan, *ins, workspace=wsf)
+        g = ba.bwd(plan, *ins, o, lse, ob, lseb, dev["do"], dev["dob"], workspace=wsb)
+        return (o, lse, ob, lseb) + tuple(g)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        static_out = step()
+    gen = torch.Generator(device="cuda")
+    for rep in range(3):
+        gen.manual_seed(1000 + rep)
+        for k in names:
+            dev[k].copy_(torch.randn(dev[k].shape, generator=gen, device="cuda").to(dev[k].dtype))
+        eager = step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(out_names, static_out, eager):
+            assert torch.equal(x, y), (rep, name)
+        say(f"  replay {rep}: bit-identical to eager")
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads: sampled rows against the row-wise oracle, plus the
 # gradient sum rules that hold at any size
