@@ -216,6 +216,83 @@ def test_forward_is_deterministic_and_stream_ordered(env):
         assert torch.equal(x, y)
 
 
+def test_invalid_calls_are_rejected_before_any_launch(env):
+    # The C ABI validates every call on the host: a bad call returns its
+    # status, names the problem in ba_last_error and writes no output. A
+    # valid call afterwards still works.
+    import ctypes
+    torch, ba = env
+    L = ba.lib()
+    w = workloads.make("dflash_r")
+    say(f"[case] invalid calls, {w.name}")
+    plan = make_plan(ba, w)
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    assert NB > 0 and plan.info["ws_fwd_bytes"] > 0
+    names = ["q", "k", "v", "qb", "kb", "vb", "do", "dob"]
+    raw, _ = inputs(w, N, NB, names=names)
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    bf = torch.bfloat16
+    out = dict(o=torch.full((N, w.hq, w.d), 7.0, dtype=bf, device="cuda"),
+               ob=torch.full((NB, w.hq, w.d), 7.0, dtype=bf, device="cuda"),
+               lse=torch.full((N, w.hq), 7.0, device="cuda"),
+               lseb=torch.full((NB, w.hq), 7.0, device="cuda"),
+               dq=torch.full((N, w.hq, w.d), 7.0, dtype=bf, device="cuda"),
+               dk=torch.full((w.C, N, w.hkv, w.d), 7.0, dtype=bf, device="cuda"),
+               dv=torch.full((w.C, N, w.hkv, w.d), 7.0, dtype=bf, device="cuda"),
+               dqb=torch.full((NB, w.hq, w.d), 7.0, dtype=bf, device="cuda"),
+               dkb=torch.full((NB, w.hkv, w.d), 7.0, dtype=bf, device="cuda"),
+               dvb=torch.full((NB, w.hkv, w.d), 7.0, dtype=bf, device="cuda"))
+    wsf = torch.empty(plan.info["ws_fwd_bytes"], dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(plan.info["ws_bwd_bytes"], dtype=torch.uint8, device="cuda")
+    p = {k: t.data_ptr() for k, t in list(dev.items()) + list(out.items())}
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def fargs(**over):
+        a = ba.FwdArgs(scale=0.0, workspace=wsf.data_ptr(), workspace_bytes=wsf.numel(),
+                       **{k: p[k] for k in ("q", "k", "v", "qb", "kb", "vb", "o", "lse", "ob",
+                                            "lseb")})
+        for k, v in over.items():
+            setattr(a, k, v)
+        return a
+
+    def bargs(**over):
+        a = ba.BwdArgs(scale=0.0, workspace=wsb.data_ptr(), workspace_bytes=wsb.numel(),
+                       dout=p["do"], doutb=p["dob"],
+                       **{k: p[k] for k in ("q", "k", "v", "qb", "kb", "vb", "o", "ob", "lse",
+                                            "lseb", "dq", "dk", "dv", "dqb", "dkb", "dvb")})
+        for k, v in over.items():
+            setattr(a, k, v)
+        return a
+
+    cases = [
+        (L.branch_attn_fwd, None, 1, "args is NULL"),
+        (L.branch_attn_fwd, fargs(workspace_bytes=wsf.numel() - 1), 3, "workspace needs"),
+        (L.branch_attn_fwd, fargs(workspace=None), 3, "workspace needs"),
+        (L.branch_attn_fwd, fargs(q=p["q"] + 2), 1, "16-byte aligned"),
+        (L.branch_attn_fwd, fargs(o=None), 1, "required"),
+        (L.branch_attn_fwd, fargs(kb=None), 1, "branch rows"),
+        (L.branch_attn_fwd, fargs(scale=float("nan")), 1, "finite"),
+        (L.branch_attn_bwd, None, 1, "args is NULL"),
+        (L.branch_attn_bwd, bargs(workspace_bytes=wsb.numel() - 1), 3, "workspace needs"),
+        (L.branch_attn_bwd, bargs(dk=p["dk"] + 8), 1, "16-byte aligned"),
+        (L.branch_attn_bwd, bargs(dout=None), 1, "required"),
+        (L.branch_attn_bwd, bargs(dvb=None), 1, "branch tensor"),
+        (L.branch_attn_bwd, bargs(scale=float("inf")), 1, "finite"),
+    ]
+    for fn, a, code, msg in cases:
+        st = fn(plan.handle, None if a is None else ctypes.byref(a), stream)
+        err = L.ba_last_error().decode()
+        assert st == code and msg in err, (fn.__name__, st, err)
+    torch.cuda.synchronize()
+    for k, t in out.items():
+        assert bool((t == 7.0).all()), f"{k} was written by a rejected call"
+    say(f"  {len(cases)} bad calls rejected, no output written")
+    assert L.branch_attn_fwd(plan.handle, ctypes.byref(fargs()), stream) == 0
+    assert L.branch_attn_bwd(plan.handle, ctypes.byref(bargs()), stream) == 0
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out["dq"].float()).all()) and not bool((out["o"] == 7.0).all())
+
+
 def test_graph_capture_replays_match_eager(env):
     # fwd + bwd enqueue kernels only (no allocation, memset or sync inside),
     # so one step can be captured in a HIP graph. Every replay, with new input
