@@ -282,35 +282,59 @@ static ba_status build(ba_plan &p, const int32_t *seqlens, const int32_t *anchor
         int32_t real_end = base;
         while (real_end < base + 2 * c && !p.is_pad[real_end]) ++real_end;
         const int32_t a_lo = seq_a0[s], a_hi = seq_a0[s + 1];
-        for (int sh = 0; sh < C; ++sh)
-          for (int half = 0; half < 2; ++half) {
-            const int32_t chunk = half == 0 ? sh : 2 * C - 1 - sh;
-            for (int32_t off = 0; off < c; off += kKTileKeys) {
-              KTile t{};
-              t.g = g;
-              t.shard = sh;
-              t.krow0 = base + half * c + off;
-              t.kpos0 = chunk * c + off;
-              t.nkeys = std::min<int32_t>(kKTileKeys, c - off);
-              // main rows with bound >= kpos0
-              const int32_t qs = int32_t(
-                  std::lower_bound(p.pos.begin() + base, p.pos.begin() + real_end, t.kpos0) -
-                  p.pos.begin());
-              t.qm_start = qs;
-              t.qm_end = std::max(qs, real_end);
-              // branch rows whose anchor position >= kpos0
-              const int32_t as = int32_t(std::lower_bound(p.anchor_pos.begin() + a_lo,
-                                                          p.anchor_pos.begin() + a_hi, t.kpos0) -
-                                         p.anchor_pos.begin());
-              t.qb_start = p.branch_off[as];
-              t.qb_end = p.branch_off[a_hi];
-              t.seq = s;
-              kt.push_back(t);
-              kc.push_back(double(t.nkeys) * G *
-                               (double(t.qm_end - t.qm_start) + double(t.qb_end - t.qb_start)) +
-                           1.0);
+        // The keys of shard sh for sequence s are its chunks sh and 2C-1-sh,
+        // stored as 2c consecutive rows. When no chunk of this rank lies
+        // between them (sh > r) and the later one holds no pad, every local
+        // row sees either all 2c keys or none, so they are cut into tiles
+        // as one run (fewer partial tiles for short chunks). A tile that
+        // spans the two chunks takes kpos0 = (its largest key position) -
+        // (nkeys - 1): the in-kernel test kpos0 + kk <= bound then holds for
+        // every key and every row in its range, as the true positions do.
+        auto emit = [&](int sh, int32_t row_off, int32_t nk, int32_t pos_first, int32_t pos_last) {
+          KTile t{};
+          t.g = g;
+          t.shard = sh;
+          t.krow0 = base + row_off;
+          t.nkeys = nk;
+          t.kpos0 = pos_last - (nk - 1);
+          // main rows with bound >= the smallest key position
+          const int32_t qs = int32_t(
+              std::lower_bound(p.pos.begin() + base, p.pos.begin() + real_end, pos_first) -
+              p.pos.begin());
+          t.qm_start = qs;
+          t.qm_end = std::max(qs, real_end);
+          // branch rows whose anchor position >= the smallest key position
+          const int32_t as = int32_t(std::lower_bound(p.anchor_pos.begin() + a_lo,
+                                                      p.anchor_pos.begin() + a_hi, pos_first) -
+                                     p.anchor_pos.begin());
+          t.qb_start = p.branch_off[as];
+          t.qb_end = p.branch_off[a_hi];
+          t.seq = s;
+          kt.push_back(t);
+          kc.push_back(double(t.nkeys) * G *
+                           (double(t.qm_end - t.qm_start) + double(t.qb_end - t.qb_start)) +
+                       1.0);
+        };
+        for (int sh = 0; sh < C; ++sh) {
+          const int32_t tail = 2 * C - 1 - sh;
+          const bool joined = sh > r && int64_t(tail + 1) * c <= p.L[s];
+          if (joined) {
+            // row i of the run: chunk sh for i < c, chunk tail after
+            auto pos_of = [&](int32_t i) { return i < c ? sh * c + i : tail * c + (i - c); };
+            for (int32_t off = 0; off < 2 * c; off += kKTileKeys) {
+              const int32_t nk = std::min<int32_t>(kKTileKeys, 2 * c - off);
+              emit(sh, off, nk, pos_of(off), pos_of(off + nk - 1));
+            }
+          } else {
+            for (int half = 0; half < 2; ++half) {
+              const int32_t chunk = half == 0 ? sh : tail;
+              for (int32_t off = 0; off < c; off += kKTileKeys) {
+                const int32_t nk = std::min<int32_t>(kKTileKeys, c - off);
+                emit(sh, half * c + off, nk, chunk * c + off, chunk * c + off + nk - 1);
+              }
             }
           }
+        }
       }
     KTile empty{};
     p.ktiles = xcd_order(kt, kc, empty);

@@ -28,9 +28,13 @@ struct QTile {
 };
 static_assert(sizeof(QTile) == 32, "QTile layout");
 
-// Key tile of the dK/dV kernel: up to kKTileKeys consecutive keys of one
-// chunk of one shard, for one kv-head, plus the local query rows that can see
-// any of them (a suffix of the sequence's main rows, and of its branch rows).
+// Key tile of the dK/dV kernel: up to kKTileKeys consecutive key rows of one
+// shard and one sequence, for one kv-head, plus the local query rows that can
+// see any of them (a suffix of the sequence's main rows, and of its branch
+// rows). The rows lie in one chunk, or span the shard's two chunks of the
+// sequence when every local row sees both chunks or neither; key kk is then
+// masked as if at position kpos0 + kk, which decides visibility exactly as
+// the true positions do.
 struct KTile {
   int32_t g, shard, krow0, kpos0;
   int32_t nkeys, qm_start, qm_end, qb_start;
