@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--cpu-anchors", type=int, default=12,
                     help="anchors in the CPU-oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-kernel event timing")
+    ap.add_argument("--mfma-probe-iters", type=int, default=200000,
+                    help="iterations of the matrix-core rate probe run after the timed steps "
+                         "(0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -232,6 +235,15 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
                 "traffic": read_traffic(dom, w.name)}
+    probe = None
+    if args.mfma_probe_iters > 0:
+        # what the matrix cores sustain on register operands on this part, zero
+        # and random data (the part is power-limited), after the timed region
+        probe = {"zero_operands_tflops": ba.probe_mfma(False, args.mfma_probe_iters),
+                 "random_operands_tflops": ba.probe_mfma(True, args.mfma_probe_iters),
+                 "iters": args.mfma_probe_iters}
+        if roof is not None:
+            probe["dominant_kernel_frac_of_random"] = roof["achieved"] / probe["random_operands_tflops"]
     cpu = None
     if args.cpu_anchors > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -255,6 +267,7 @@ def main():
         "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "mfma_probe": probe,
         "kernels": kernels,
         "wall_s": wall,
     }

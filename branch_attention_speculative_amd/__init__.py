@@ -112,6 +112,9 @@ def lib():
         L.ba_profile_read.restype = ctypes.c_int
         L.ba_profile_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int32)]
+        L.ba_probe_mfma.restype = ctypes.c_int
+        L.ba_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
         _lib = L
     return _lib
 
@@ -354,3 +357,19 @@ def _autograd():
 def branch_attention(plan, q, k, v, qb=None, kb=None, vb=None, scale=0.0):
     """Differentiable branch attention (torch.autograd); returns (o, ob)."""
     return _autograd().apply(plan, scale, q, k, v, qb, kb, vb)
+
+
+def probe_mfma(random_operands=True, iters=20000, device=None):
+    """Dense bf16 MFMA rate (TFLOP/s) that the part sustains on register
+    operands: all zero, or pseudo-random values that change every MFMA.
+    Synchronises. A measurement aid, not part of the attention path."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    sink = torch.empty(8192, dtype=torch.float32, device=dev)
+    out = ctypes.c_double(0.0)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _check(lib().ba_probe_mfma(1 if random_operands else 0, int(iters), ctypes.c_void_p(sink.data_ptr()),
+                                   sink.numel(), ctypes.c_void_p(stream), ctypes.byref(out)),
+               "ba_probe_mfma")
+    return out.value

@@ -25,7 +25,8 @@ CFLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["plan.cpp", "api.hip", "fwd_ring.hip", "bwd_ring.hip", "branch.hip", "ring_f32.hip"]
+SOURCES = ["plan.cpp", "api.hip", "fwd_ring.hip", "bwd_ring.hip", "branch.hip", "ring_f32.hip",
+           "probe.hip"]
 
 
 def _compile(src):

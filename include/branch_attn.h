@@ -225,6 +225,24 @@ typedef struct {
 ba_status ba_profile_enable(int32_t on, int32_t max_launches);
 ba_status ba_profile_read(ba_kernel_time *out, int32_t max_entries, int32_t *n_entries);
 
+/*
+ * Matrix-core rate probe (measurement aid, not part of the attention path;
+ * for callers that compare kernel rates with what the part sustains). Every
+ * wave of a grid of 2048 x 256 threads runs eight independent accumulation
+ * chains of bf16 32x32x16 MFMAs on register operands for `iters` iterations:
+ * all-zero operands (random_operands = 0) or fixed pseudo-random bf16 values
+ * in [-1, 1) that change from one MFMA to the next (random_operands != 0).
+ *   sink     device buffer of at least 8192 floats (per-wave sums, written so
+ *            the work is kept); sink_len its length in floats.
+ *   stream   enqueued on this stream; the call then synchronises on it (unlike
+ *            fwd/bwd) and creates and destroys two HIP events.
+ *   *tflops  dense bf16 TFLOP/s measured with HIP events around the launch.
+ * Returns BA_E_INVALID for a NULL sink/tflops, iters outside 1..2^24 or a
+ * short sink, BA_E_HIP if a HIP call fails.
+ */
+ba_status ba_probe_mfma(int32_t random_operands, int32_t iters, float *sink, int64_t sink_len,
+                        void *stream, double *tflops);
+
 #ifdef __cplusplus
 }
 #endif
