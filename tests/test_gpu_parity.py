@@ -159,6 +159,9 @@ EDGES = [
     _edge("block-empty", [64, 64], 4, 3, pack.KIND_BLOCK_BIDIR, 16, 8, 2, anchors=[0], blens=[4]),
     # a long single chunk: several key blocks per shard, ragged tails
     _edge("ragged", [1999], 3, 1, pack.KIND_TTT, 2, 8, 2),
+    # the largest CP degree the planner accepts: 128 chunks per sequence,
+    # chunks of a few rows, a rank in the middle
+    _edge("c64", [1000, 300, 2], 64, 37, pack.KIND_TTT, 2, 8, 2),
 ]
 
 

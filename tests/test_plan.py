@@ -78,6 +78,18 @@ def test_plan_matches_oracle_every_rank_small():
             _compare(w, r)
 
 
+@pytest.mark.parametrize("C,r", [(16, 15), (33, 7), (64, 0), (64, 63)])
+def test_plan_matches_oracle_at_large_cp_degree(C, r):
+    # up to the largest CP degree the planner accepts; short and long
+    # sequences, so that some chunks are one row or all pads
+    for kind, depth, anchors, blens in ((pack.KIND_TTT, 3, None, None),
+                                        (pack.KIND_BLOCK_CAUSAL, 0, [0, 500, 1499, 1600], [4, 64, 1, 9])):
+        w = workloads.Workload("bigc", [1500, 7, 2 * C + 1, 130], C, r, kind, depth, 8, 2, 128, "bf16",
+                               True, 0, anchors=anchors, branch_lens=blens)
+        p, lay, br = _compare(w)
+        _check_worklists(p, lay, br, w)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_plan_matches_oracle_random(seed):
     rng = np.random.default_rng(1000 + seed)
