@@ -162,6 +162,9 @@ EDGES = [
     # the largest CP degree the planner accepts: 128 chunks per sequence,
     # chunks of a few rows, a rank in the middle
     _edge("c64", [1000, 300, 2], 64, 37, pack.KIND_TTT, 2, 8, 2),
+    # many short sequences: hundreds of per-sequence tiles, chunks of 1-10 rows
+    _edge("many-seqs", [int(x) for x in np.random.default_rng(5).integers(1, 41, size=150)], 2, 1,
+          pack.KIND_TTT, 3, 8, 2),
 ]
 
 
