@@ -118,6 +118,18 @@ def test_fp32_forward_backward(env, kind, d, C):
     _check_bwd(w, got, ref)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp32_at_reduced_workload_size(env, d):
+    # the fp32 path beyond tiny inputs: the sequences of the reduced ttt32k
+    # workload (four, about 3,300 tokens, C=4, TTT depth 7) in fp32, 8/2 heads
+    base = workloads.make("ttt32k_r")
+    w = workloads.Workload(f"ttt32k_r-fp32-d{d}", base.seqlens, base.C, base.r, base.kind,
+                           base.depth_or_block, 8, 2, d, "fp32", True, base.seed)
+    got, ref, _ = _run(env, w, with_bwd=True, oracle_dtype=np.float64)
+    _check_fwd(w, got, ref)
+    _check_bwd(w, got, ref)
+
+
 @pytest.mark.parametrize("name", ["ttt32k_r", "dflash_r", "long256k_r", "dspark_r"])
 def test_reduced_workloads(env, name):
     w = workloads.make(name)
