@@ -383,6 +383,81 @@ def _sample_rows(lay, br, rng, n_main, n_anchor):
     return sorted(rows), brows
 
 
+class _DeviceRows:
+    """Row access to a device tensor for the row-sampled oracle: indexing
+    copies only the requested rows to the host, as float32."""
+
+    def __init__(self, torch, t):
+        self.torch, self.t, self.shape = torch, t, tuple(t.shape)
+
+    def __getitem__(self, idx):
+        def dev(i):
+            return self.torch.as_tensor(i, device=self.t.device) if isinstance(i, np.ndarray) else i
+        idx = tuple(dev(i) for i in idx) if isinstance(idx, tuple) else dev(idx)
+        return self.t[idx].float().cpu().numpy()
+
+
+def test_element_offsets_beyond_2_31(env):
+    """Branch tensors with more than 2^31 elements: one 40,960-token sequence,
+    C=1, EAGLE-3 TTT depth 7 (286,720 branch rows), 64/8 heads, d=128, bf16.
+    The inputs are drawn on the device (seeded); the last anchors' rows, whose
+    element offsets lie beyond 2^31, are checked against the row-wise oracle,
+    plus the dK/dV sum rules over the whole tensors."""
+    torch, ba = env
+    w = workloads.Workload("offsets64", [40960], 1, 0, pack.KIND_TTT, 7, 64, 8, 128, "bf16", True, 31)
+    say(f"[case] {w.name}: 40960 tokens, C=1, TTT depth 7, 64/8 heads")
+    lay, br = oracle_structs(w)
+    plan = make_plan(ba, w)
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    assert NB * w.hq * w.d > 2 ** 31
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(31)
+    shapes = dict(q=(N, w.hq, w.d), k=(w.C, N, w.hkv, w.d), v=(w.C, N, w.hkv, w.d),
+                  qb=(NB, w.hq, w.d), kb=(NB, w.hkv, w.d), vb=(NB, w.hkv, w.d),
+                  do=(N, w.hq, w.d), dob=(NB, w.hq, w.d))
+    dev = {k: torch.randn(shp, device="cuda", dtype=torch.bfloat16, generator=gen)
+           for k, shp in shapes.items()}
+    o, lse, ob, lseb = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+    dq, dk, dv, dqb, dkb, dvb = ba.bwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"],
+                                       dev["vb"], o, lse, ob, lseb, dev["do"], dev["dob"])
+    torch.cuda.synchronize()
+    say("  device pass done")
+    # the first and last main rows, and every branch row of the first and last
+    # three anchors
+    rows = [0, 1, N // 2, N - 2, N - 1]
+    A = br["anchor_row"].size
+    brows = []
+    for a in [0, A - 3, A - 2, A - 1]:
+        brows += list(range(int(br["branch_off"][a]), int(br["branch_off"][a + 1])))
+    assert max(brows) * w.hq * w.d > 2 ** 31
+    host = {k: dev[k].float().cpu().numpy() for k in ("k", "v")}
+    R = {k: _DeviceRows(torch, dev[k]) for k in ("q", "qb", "kb", "vb", "do", "dob")}
+    ref = attn.attn_rows(lay, br, R["q"], host["k"], host["v"], R["qb"], R["kb"], R["vb"], rows,
+                         brows, dtype=np.float32, do=R["do"], dob=R["dob"])
+    ri = torch.tensor(rows, device="cuda")
+    bi = torch.tensor(brows, device="cuda", dtype=torch.long)
+    for nm, go, gl, gd, key, idx in (("main", o, lse, dq, "main", rows), ("branch", ob, lseb, dqb, "branch", brows)):
+        sel = ri if nm == "main" else bi
+        wo = np.stack([ref[key][r]["o"] for r in idx])
+        wl = np.stack([ref[key][r]["lse"] for r in idx])
+        wd = np.stack([ref[key][r]["dq"] for r in idx])
+        e_o, r_o, e_l = max_abs(to_host(go[sel]), wo), rel_l2(to_host(go[sel]), wo), lse_err(to_host(gl[sel]), wl)
+        ok, ma, rl = grad_ok(to_host(gd[sel]), wd, True)
+        say(f"  {nm}: max|dO|={e_o:.3e} relL2={r_o:.3e} max|dLSE|={e_l:.3e} dq max-abs={ma:.3e} relL2={rl:.3e}")
+        assert e_o <= 2e-2 and r_o <= 1e-2 and e_l <= 1e-3 and ok
+    G = w.hq // w.hkv
+    do_sum = dev["do"].float().view(-1, w.hkv, G, w.d).sum(dim=(0, 2)) + \
+        dev["dob"].float().view(NB, w.hkv, G, w.d).sum(dim=(0, 2))
+    dv_sum = dv.float().sum(dim=(0, 1)) + dvb.float().sum(dim=0)
+    dk_sum = dk.float().sum(dim=(0, 1)) + dkb.float().sum(dim=0)
+    dv_mag = dv.float().abs().sum(dim=(0, 1)) + dvb.float().abs().sum(dim=0)
+    dk_mag = dk.float().abs().sum(dim=(0, 1)) + dkb.float().abs().sum(dim=0)
+    ev = float(((dv_sum - do_sum).abs() / dv_mag.clamp_min(1e-6)).max())
+    ek = float((dk_sum.abs() / dk_mag.clamp_min(1e-6)).max())
+    say(f"  sum rules: |sum dV - sum dO|/sum|dV| = {ev:.3e}, |sum dK|/sum|dK| = {ek:.3e}")
+    assert ev <= 1e-2 and ek <= 1e-2
+
+
 @pytest.mark.parametrize("name", ["ttt32k", "dflash", "dspark", "long256k"])
 def test_full_size_sampled(env, name):
     torch, ba = env
