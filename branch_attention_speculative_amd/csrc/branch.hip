@@ -293,13 +293,13 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
   const T *DOB = static_cast<const T *>(a.doutb);
   stage_branch_kv<T, DIM>(static_cast<const T *>(a.kb), static_cast<const T *>(a.vb), base, t.rows,
                           t.g, a.hkv, sK, sV);
-  // phase-2 items: (key row kl, 4 consecutive d) -> fixed per thread
-  constexpr int ITEMS = (kMaxBranch * DIM / 4 + 255) / 256;
-  float adk[ITEMS][4], adv[ITEMS][4];
+  // phase-2 items: (key row kl, 8 consecutive d) -> fixed per thread
+  constexpr int ITEMS = (kMaxBranch * DIM / 8 + 255) / 256;
+  float adk[ITEMS][8], adv[ITEMS][8];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) adk[it][e] = adv[it][e] = 0.f;
+    for (int e = 0; e < 8; ++e) adk[it][e] = adv[it][e] = 0.f;
   const int nqv = t.rows * G;
   // phase 1: four threads per query vector of the chunk, each over a quarter of D
   const int ql = tid >> 2, sub = tid & 3;
@@ -393,8 +393,8 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
       const int item = tid + 256 * it;
-      if (item < t.rows * (DIM / 4)) {
-        const int kl = item / (DIM / 4), d4 = item % (DIM / 4);
+      if (item < t.rows * (DIM / 8)) {
+        const int kl = item / (DIM / 8), d4 = item % (DIM / 8);
         const int an = a.b_anchor[base + kl];
         const int lo = a.branch_off[an] - base;
         const int hi = a.branch_off[an + 1] - base;
@@ -404,11 +404,11 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
           const float p = sP[(qv - c0) * MAXB + kl - lo];
           const float d = sS[(qv - c0) * MAXB + kl - lo];
           if (p == 0.f && d == 0.f) continue;
-          float q4[4], o4[4];
-          ld4<T>(sQ, (qv - c0) * DIM + d4 * 4, q4);
-          ld4<T>(sDO, (qv - c0) * DIM + d4 * 4, o4);
+          float q4[8], o4[8];
+          ld8<T>(sQ, (qv - c0) * DIM + d4 * 8, q4);
+          ld8<T>(sDO, (qv - c0) * DIM + d4 * 8, o4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 8; ++e) {
             adk[it][e] = fmaf(d, q4[e], adk[it][e]);
             adv[it][e] = fmaf(p, o4[e], adv[it][e]);
           }
@@ -421,11 +421,11 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int item = tid + 256 * it;
-    if (item < t.rows * (DIM / 4)) {
-      const int kl = item / (DIM / 4), d4 = item % (DIM / 4);
-      const int64_t off = (int64_t(base + kl) * a.hkv + t.g) * DIM + d4 * 4;
+    if (item < t.rows * (DIM / 8)) {
+      const int kl = item / (DIM / 8), d4 = item % (DIM / 8);
+      const int64_t off = (int64_t(base + kl) * a.hkv + t.g) * DIM + d4 * 8;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 8; ++e) {
         if constexpr (sizeof(T) == 2) {
           DKB[off + e] = f2bf(adk[it][e] * a.scale);
           DVB[off + e] = f2bf(adv[it][e]);
