@@ -134,7 +134,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="long256k", choices=workloads.ALL)
-    ap.add_argument("--cpu-anchors", type=int, default=12,
+    ap.add_argument("--cpu-anchors", type=int, default=10,
                     help="anchors in the CPU-oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-kernel event timing")
     ap.add_argument("--mfma-probe-iters", type=int, default=200000,
