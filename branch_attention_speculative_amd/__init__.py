@@ -239,6 +239,19 @@ def _expect(name, t, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _workspace(ws, need, device):
+    """Byte size of a caller-supplied workspace after checking that it is a
+    contiguous tensor on the right device (its dtype does not matter)."""
+    if ws.device != device:
+        raise ValueError(f"workspace: expected device {device}, got {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace: needs {need} bytes, got {nbytes}")
+    return nbytes
+
+
 def _shapes(plan):
     i = plan.info
     N, NB, C = i["n_local_rows"], i["n_branch_rows"], i["cp_degree"]
@@ -271,7 +284,7 @@ def fwd(plan, q, k, v, qb=None, kb=None, vb=None, scale=0.0, workspace=None):
     a = FwdArgs(scale=float(scale), q=_ptr(q), k=_ptr(k), v=_ptr(v), qb=_ptr(qb), kb=_ptr(kb),
                 vb=_ptr(vb), o=_ptr(o), lse=_ptr(lse), ob=_ptr(ob), lseb=_ptr(lseb),
                 workspace=_ptr(workspace),
-                workspace_bytes=0 if workspace is None else workspace.numel())
+                workspace_bytes=0 if workspace is None else _workspace(workspace, ws_bytes, dev))
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         _check(lib().branch_attn_fwd(plan.handle, ctypes.byref(a), ctypes.c_void_p(stream)),
@@ -307,7 +320,7 @@ def bwd(plan, q, k, v, qb, kb, vb, o, lse, ob, lseb, do, dob, scale=0.0, workspa
                 vb=_ptr(vb), o=_ptr(o), ob=_ptr(ob), lse=_ptr(lse), lseb=_ptr(lseb),
                 dout=_ptr(do), doutb=_ptr(dob), dq=_ptr(dq), dk=_ptr(dk), dv=_ptr(dv),
                 dqb=_ptr(dqb), dkb=_ptr(dkb), dvb=_ptr(dvb), workspace=_ptr(workspace),
-                workspace_bytes=workspace.numel())
+                workspace_bytes=_workspace(workspace, plan.info["ws_bwd_bytes"], dev))
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         _check(lib().branch_attn_bwd(plan.handle, ctypes.byref(a), ctypes.c_void_p(stream)),

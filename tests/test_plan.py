@@ -228,3 +228,16 @@ def test_fwd_without_upload_is_rejected_before_any_device_call():
     st = ba.lib().branch_attn_fwd(p.handle, a, None)
     assert ba.lib().ba_status_str(st) == b"BA_E_INVALID"
     assert b"not uploaded" in ba.lib().ba_last_error()
+
+
+def test_binding_checks_the_caller_workspace():
+    torch = pytest.importorskip("torch")
+    cpu = torch.device("cpu")
+    # the size is counted in bytes, whatever the dtype
+    assert ba._workspace(torch.empty(16, dtype=torch.float32), 64, cpu) == 64
+    with pytest.raises(ValueError, match="needs 65 bytes"):
+        ba._workspace(torch.empty(16, dtype=torch.float32), 65, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        ba._workspace(torch.empty(8, 8, dtype=torch.uint8).t(), 1, cpu)
+    with pytest.raises(ValueError, match="expected device"):
+        ba._workspace(torch.empty(8, dtype=torch.uint8), 1, torch.device("cuda", 0))
