@@ -234,6 +234,30 @@ def test_forward_is_deterministic_and_stream_ordered(env):
         assert torch.equal(x, y)
 
 
+def test_autograd_wrapper_matches_the_direct_calls(env):
+    # branch_attention() under torch.autograd: the gradients that backward()
+    # produces for a loss <O, dO> + <Ob, dOb> are exactly those of bwd()
+    torch, ba = env
+    w = workloads.make("dflash_r")
+    say(f"[case] autograd wrapper, {w.name}")
+    plan = make_plan(ba, w)
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    raw, _ = inputs(w, N, NB)
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    names = ("q", "k", "v", "qb", "kb", "vb")
+    leaves = {k: dev[k].clone().requires_grad_(True) for k in names}
+    o, ob = ba.branch_attention(plan, *(leaves[k] for k in names))
+    loss = (o.float() * dev["do"].float()).sum() + (ob.float() * dev["dob"].float()).sum()
+    loss.backward()
+    ref_o, ref_lse, ref_ob, ref_lseb = ba.fwd(plan, *(dev[k] for k in names))
+    ref = ba.bwd(plan, *(dev[k] for k in names), ref_o, ref_lse, ref_ob, ref_lseb, dev["do"],
+                 dev["dob"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), ref_o) and torch.equal(ob.detach(), ref_ob)
+    for k, g in zip(names, ref):
+        assert torch.equal(leaves[k].grad, g), k
+
+
 def test_invalid_calls_are_rejected_before_any_launch(env):
     # The C ABI validates every call on the host: a bad call returns its
     # status, names the problem in ba_last_error and writes no output. A
