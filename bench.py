@@ -16,6 +16,7 @@ depth 7), 32 q-heads / 8 kv-heads, d=128, bf16.
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -134,6 +135,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="long256k", choices=workloads.ALL)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="with the long256k workload: another sequence length (same CP degree, "
+                         "TTT depth and heads), for length sweeps")
     ap.add_argument("--cpu-anchors", type=int, default=10,
                     help="anchors in the CPU-oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--no-profile", action="store_true", help="skip per-kernel event timing")
@@ -158,6 +162,11 @@ def main():
         sys.exit(1)
 
     w = workloads.make(args.workload)
+    if args.tokens:
+        if args.workload != "long256k":
+            print("--tokens applies to the long256k workload only", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, name=f"ttt{args.tokens}", seqlens=[args.tokens])
     plan = ba.Plan(w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.anchors, w.branch_lens,
                    w.hq, w.hkv, w.d, w.dtype).upload()
     info = plan.info
