@@ -40,7 +40,10 @@ kb, vb [N_b, Hkv, D]; lse [rows, Hq] natural log.
 
 Parity: pinned (tests/test_oracle_attn.py: pure-Python brute force on the
 unpermuted batch, torch SDPA reduction, K = 0 closed form, one-hot V, finite
-differences, fp32 vs fp64 bound, gradient sum rules, split = unsplit).
+differences, fp32 vs fp64 bound, gradient sum rules, split = unsplit). The
+row-sampled form ``attn_rows`` (o, lse, dq and its dK/dV accumulation) and the
+subset form ``attn_subset`` (every output) are pinned against the dense
+``attn_fwd``/``attn_bwd`` on every row of small cases.
 """
 
 import numpy as np
@@ -378,3 +381,115 @@ def attn_rows(layout, br, q, k, v, qb, kb, vb, main_rows=(), branch_rows=(),
                     dv_acc[s][:n, g] += P[:, :n].T @ dOg
         out[kind_row][row] = res
     return out
+
+
+# ---------------------------------------------------------------------------
+# A subset of a rank's rows in the dense masked form.
+
+
+def attn_subset(layout, br, q, k, v, qb, kb, vb, main_rows=(), anchors=(), do=None, dob=None,
+                scale=None, dtype=np.float32, row_block=512):
+    """Dense masked forward (and with ``do``/``dob`` the backward) of a subset
+    of the rank's rows: the given main rows and every branch row of the given
+    local anchors, each against its whole visible key set, by the definitions
+    of ``attn_fwd``/``attn_bwd``. The key list of a sequence holds its main
+    keys at positions 0 .. (largest bound among the selected rows) and the
+    branch keys of the selected anchors; keys beyond it are seen by none of
+    the selected rows. Rows are taken in blocks of ``row_block``.
+
+    Returns a dict: 'main_rows', 'branch_rows' (the row indices, in the order
+    of the outputs), 'o', 'lse', 'dq' [len(main_rows), Hq, D], 'ob', 'lseb',
+    'dqb' for the branch rows, and the subset's contributions to the key
+    gradients 'dk', 'dv' [C, N_loc, Hkv, D] and 'dkb', 'dvb' [N_b, Hkv, D].
+    Pad rows get O = 0 and LSE = -inf."""
+    N, Hq, D = q.shape
+    C, Nl, Hkv, _ = k.shape
+    G = Hq // Hkv
+    sc = dtype(_scale(D, scale))
+    kind = br["kind"]
+    want_bwd = do is not None
+    main_rows = np.asarray(main_rows, np.int64)
+    anchors = np.asarray(anchors, np.int64)
+    branch_rows = (np.concatenate([np.arange(br["branch_off"][a], br["branch_off"][a + 1])
+                                   for a in anchors]).astype(np.int64)
+                   if anchors.size else np.zeros(0, np.int64))
+    res = {"main_rows": main_rows, "branch_rows": branch_rows,
+           "o": np.zeros((main_rows.size, Hq, D), dtype),
+           "lse": np.full((main_rows.size, Hq), -np.inf, dtype),
+           "ob": np.zeros((branch_rows.size, Hq, D), dtype),
+           "lseb": np.full((branch_rows.size, Hq), -np.inf, dtype)}
+    if want_bwd:
+        res.update(dq=np.zeros((main_rows.size, Hq, D), dtype),
+                   dqb=np.zeros((branch_rows.size, Hq, D), dtype),
+                   dk=np.zeros((C, Nl, Hkv, D), dtype), dv=np.zeros((C, Nl, Hkv, D), dtype),
+                   dkb=np.zeros((br["n_branch"], Hkv, D), dtype),
+                   dvb=np.zeros((br["n_branch"], Hkv, D), dtype))
+    # output slot of every selected row: main rows first, then branch rows
+    for s in range(layout["L"].size):
+        mi = np.nonzero((layout["seq"][main_rows] == s) & (layout["is_pad"][main_rows] == 0))[0]
+        bi = np.nonzero(br["anchor_seq"][br["b_anchor"][branch_rows]] == s)[0] \
+            if branch_rows.size else np.zeros(0, np.int64)
+        if mi.size + bi.size == 0:
+            continue
+        qrows_m = main_rows[mi]
+        qrows_b = branch_rows[bi]
+        bounds = np.concatenate([layout["pos"][qrows_m],
+                                 br["anchor_pos"][br["b_anchor"][qrows_b]]]).astype(np.int64)
+        n_main = int(bounds.max()) + 1
+        shard_of, row_of = _seq_main_key_index(layout, s)
+        ksh, krow = shard_of[:n_main], row_of[:n_main]
+        kbr = qrows_b  # branch keys are stored row-for-row with branch queries
+        Q = np.concatenate([q[qrows_m].astype(dtype), qb[qrows_b].astype(dtype)], axis=0)
+        K = np.concatenate([k[ksh, krow].astype(dtype), kb[kbr].astype(dtype)], axis=0)
+        V = np.concatenate([v[ksh, krow].astype(dtype), vb[kbr].astype(dtype)], axis=0)
+        if want_bwd:
+            dO = np.concatenate([do[qrows_m].astype(dtype), dob[qrows_b].astype(dtype)], axis=0)
+        key_pos = np.arange(n_main)
+        # per query: its bound, and for branch rows its anchor and step
+        q_is_branch = np.concatenate([np.zeros(qrows_m.size, bool), np.ones(qrows_b.size, bool)])
+        q_anchor = np.concatenate([np.full(qrows_m.size, -1), br["b_anchor"][qrows_b]])
+        q_j = np.concatenate([np.full(qrows_m.size, -1), br["b_j"][qrows_b]])
+        k_anchor = br["b_anchor"][kbr]
+        k_j = br["b_j"][kbr]
+        nq = Q.shape[0]
+        for r0 in range(0, nq, row_block):
+            r1 = min(nq, r0 + row_block)
+            mask = np.zeros((r1 - r0, n_main + kbr.size), dtype=bool)
+            for i in range(r0, r1):
+                mask[i - r0, :n_main] = key_pos <= bounds[i]
+                if q_is_branch[i]:
+                    same = k_anchor == q_anchor[i]
+                    if kind == _pack.KIND_BLOCK_BIDIR:
+                        vis = same
+                    else:
+                        vis = same & (k_j <= q_j[i])
+                    mask[i - r0, n_main:] = vis
+            for h in range(Hq):
+                g = h // G
+                S = (Q[r0:r1, h] @ K[:, g].T) * sc
+                l_, P = _masked_softmax(S, mask)
+                O = P @ V[:, g]
+                for i in range(r0, r1):
+                    slot_o, slot_l = (("o", "lse") if not q_is_branch[i] else ("ob", "lseb"))
+                    j = mi[i] if not q_is_branch[i] else bi[i - qrows_m.size]
+                    res[slot_o][j, h] = O[i - r0]
+                    res[slot_l][j, h] = l_[i - r0]
+                if not want_bwd:
+                    continue
+                dOh = dO[r0:r1, h]
+                delta = np.sum(dOh * O, axis=-1, keepdims=True)
+                dP = dOh @ V[:, g].T
+                dS = P * (dP - delta)
+                dQ = (dS @ K[:, g]) * sc
+                dK = (dS.T @ Q[r0:r1, h]) * sc
+                dV = P.T @ dOh
+                for i in range(r0, r1):
+                    if not q_is_branch[i]:
+                        res["dq"][mi[i], h] = dQ[i - r0]
+                    else:
+                        res["dqb"][bi[i - qrows_m.size], h] = dQ[i - r0]
+                res["dk"][ksh, krow, g] += dK[:n_main]
+                res["dv"][ksh, krow, g] += dV[:n_main]
+                res["dkb"][kbr, g] += dK[n_main:]
+                res["dvb"][kbr, g] += dV[n_main:]
+    return res

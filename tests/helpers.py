@@ -101,3 +101,131 @@ class LazyF32:
 
     def __getitem__(self, idx):
         return workloads.as_f32(self.w, self.raw[idx])
+
+
+def shift_late_keys(lam):
+    """Input preparation: add lam * u (u a fixed unit vector) to every main key
+    in the second half of its sequence. A query's scores against those keys
+    move by lam * scale * <q, u> together: for queries with <q, u> > 0 they
+    jump far above the scores of earlier keys, for <q, u> < 0 they fall far
+    below them. Inside each half the attention stays as diffuse as with plain
+    N(0, 1) data. Keys that share a large component are also the input domain
+    where a bf16 backward loses accuracy (the rounding errors of dS and Delta
+    are multiplied by that component in dQ = scale dS K)."""
+    def prep(w, lay, raw):
+        k = workloads.as_f32(w, raw["k"]).copy()
+        u = np.random.default_rng(99).standard_normal(w.d).astype(np.float32)
+        u /= np.linalg.norm(u)
+        for s_ in range(w.C):
+            ls = pack.zigzag_layout(w.seqlens, w.C, s_)
+            late = ls["pos"] >= (ls["L"][ls["seq"]] + 1) // 2
+            k[s_][late] += lam * u
+        raw["k"] = workloads.f32_to_bf16_bits(k) if w.dtype == "bf16" else k
+    return prep
+
+
+def oracle_grouped(lay, br, q, k, v, qb, kb, vb, do=None, dob=None, dtype=np.float32,
+                   threads=4, log=None):
+    """The oracle's dense forward (and with do/dob its backward), evaluated one
+    kv-group at a time on a thread pool: the oracle's heads are independent,
+    and a group's q-heads see only that group's K/V, so calling it on the
+    group's slices gives exactly its full-tensor result. Returns a dict with
+    o, lse, ob, lseb (and dq, dk, dv, dqb, dkb, dvb)."""
+    import concurrent.futures
+    Hq, Hkv = q.shape[1], k.shape[2]
+    G = Hq // Hkv
+    want_bwd = do is not None
+
+    def one(g):
+        hs = slice(g * G, (g + 1) * G)
+        gs = slice(g, g + 1)
+        ins = (q[:, hs], k[:, :, gs], v[:, :, gs], qb[:, hs], kb[:, gs], vb[:, gs])
+        res = dict(zip(("o", "lse", "ob", "lseb"), attn.attn_fwd(lay, br, *ins, dtype=dtype)))
+        if want_bwd:
+            res.update(zip(("dq", "dk", "dv", "dqb", "dkb", "dvb"),
+                           attn.attn_bwd(lay, br, *ins, do[:, hs], dob[:, hs], dtype=dtype)))
+        if log is not None:
+            log(f"  oracle kv-group {g} done")
+        return g, res
+
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        parts = dict(ex.map(one, range(Hkv)))
+    out = {}
+    for name in parts[0]:
+        axis = {"dk": 2, "dv": 2, "dkb": 1, "dvb": 1}.get(name, 1)
+        out[name] = np.concatenate([parts[g][name] for g in range(Hkv)], axis=axis)
+    return out
+
+
+class HeadSlice:
+    """Row access to an input whose head axis (second to last) is restricted
+    to ``hs``: indexing gathers the rows first, then slices the heads, so
+    encoded full-size inputs are decoded only where they are read."""
+
+    def __init__(self, arr, hs):
+        self.arr, self.hs = arr, hs
+        shp = list(arr.shape)
+        shp[-2] = len(range(*hs.indices(shp[-2])))
+        self.shape = tuple(shp)
+
+    def __getitem__(self, idx):
+        return self.arr[idx][..., self.hs, :]
+
+
+def subset_grouped(lay, br, q, k, v, qb, kb, vb, main_rows, anchors, do=None, dob=None,
+                   threads=8, log=None):
+    """``attn.attn_subset`` evaluated one kv-group at a time on a thread pool
+    (heads are independent; a group's q-heads see only its K/V). Inputs may be
+    any row-indexable arrays (LazyF32 for encoded full-size tensors)."""
+    import concurrent.futures
+    Hq, Hkv = q.shape[1], k.shape[2]
+    G = Hq // Hkv
+    want_bwd = do is not None
+
+    def one(g):
+        hs, gs = slice(g * G, (g + 1) * G), slice(g, g + 1)
+        r = attn.attn_subset(lay, br, HeadSlice(q, hs), HeadSlice(k, gs), HeadSlice(v, gs),
+                             HeadSlice(qb, hs), HeadSlice(kb, gs), HeadSlice(vb, gs),
+                             main_rows=main_rows, anchors=anchors,
+                             do=HeadSlice(do, hs) if want_bwd else None,
+                             dob=HeadSlice(dob, hs) if want_bwd else None)
+        if log is not None:
+            log(f"  oracle kv-group {g} done")
+        return g, r
+
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        parts = dict(ex.map(one, range(Hkv)))
+    out = {"main_rows": parts[0]["main_rows"], "branch_rows": parts[0]["branch_rows"]}
+    for name in parts[0]:
+        if name in out:
+            continue
+        axis = {"dk": 2, "dv": 2, "dkb": 1, "dvb": 1}.get(name, 1)
+        out[name] = np.concatenate([parts[g][name] for g in range(Hkv)], axis=axis)
+    return out
+
+
+def complete_keys(lay, br, main_rows, anchors):
+    """Main keys (per sequence, positions >= p*) and branch keys whose every
+    viewer among the rank's rows is in the subset, so that the subset's dK/dV
+    contributions are their whole gradient. Returns (boolean mask over
+    [C, N_loc] shard rows, boolean mask over branch rows)."""
+    C = lay["C"]
+    sel_m = np.zeros(lay["n_local"], bool)
+    sel_m[np.asarray(main_rows, np.int64)] = True
+    A = br["anchor_row"].size
+    sel_a = np.zeros(A, bool)
+    sel_a[np.asarray(anchors, np.int64)] = True
+    S = lay["L"].size
+    pstar = np.zeros(S, np.int64)
+    for i in np.nonzero(~sel_m & (lay["is_pad"] == 0))[0]:
+        s = lay["seq"][i]
+        pstar[s] = max(pstar[s], lay["pos"][i] + 1)
+    for a in np.nonzero(~sel_a)[0]:
+        s = br["anchor_seq"][a]
+        pstar[s] = max(pstar[s], br["anchor_pos"][a] + 1)
+    keys = np.zeros((C, lay["n_local"]), bool)
+    for sh in range(C):
+        ls = pack.zigzag_layout(lay["L"].tolist(), C, sh)
+        keys[sh] = (ls["is_pad"] == 0) & (ls["pos"] >= pstar[ls["seq"]])
+    bkeys = sel_a[br["b_anchor"]] if br["n_branch"] else np.zeros(0, bool)
+    return keys, bkeys

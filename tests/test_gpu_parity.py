@@ -11,14 +11,16 @@ The rel-L2 guard on O matters at long context, where |O| itself shrinks
 towards 2e-2 and a max-abs bound alone would accept O = 0.
 """
 
+import time
+
 import numpy as np
 import pytest
 
 import workloads
 from oracle import attn, pack
 
-from helpers import LazyF32, grad_ok, inputs, lse_err, make_plan, max_abs, oracle_structs, \
-    rel_l2, say, to_device, to_host
+from helpers import LazyF32, complete_keys, grad_ok, inputs, lse_err, make_plan, max_abs, \
+    oracle_grouped, oracle_structs, rel_l2, say, shift_late_keys, subset_grouped, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +35,7 @@ def env():
     return torch, ba
 
 
-def _run(env, w, with_bwd, oracle_dtype=np.float32, prep=None):
+def _run(env, w, with_bwd, oracle_dtype=np.float32, prep=None, threads=4):
     torch, ba = env
     say(f"[case] {w.name}: lens={w.seqlens[:6]}{'...' if len(w.seqlens) > 6 else ''} C={w.C} r={w.r} "
         f"kind={w.kind} depth/block={w.depth_or_block} heads={w.hq}/{w.hkv} d={w.d} {w.dtype}")
@@ -55,10 +57,8 @@ def _run(env, w, with_bwd, oracle_dtype=np.float32, prep=None):
     torch.cuda.synchronize()
     got = {k: to_host(v) for k, v in res.items()}
     ins = [dec[k] for k in ("q", "k", "v", "qb", "kb", "vb")]
-    ref = dict(zip(("o", "lse", "ob", "lseb"), attn.attn_fwd(lay, br, *ins, dtype=oracle_dtype)))
-    if with_bwd:
-        ref.update(zip(("dq", "dk", "dv", "dqb", "dkb", "dvb"),
-                       attn.attn_bwd(lay, br, *ins, dec["do"], dec["dob"], dtype=oracle_dtype)))
+    ref = oracle_grouped(lay, br, *ins, dec["do"] if with_bwd else None,
+                         dec["dob"] if with_bwd else None, dtype=oracle_dtype, threads=threads)
     return got, ref, plan
 
 
@@ -187,35 +187,35 @@ def test_edge_cases(env, w):
     _check_bwd(w, got, ref)
 
 
-def _shift_late_keys(lam):
-    """Add lam * u (u a fixed unit vector) to every main key in the second
-    half of its sequence. A query's scores against those keys move by
-    lam * scale * <q, u> together: for queries with <q, u> > 0 they jump far
-    above the running max taken from earlier key blocks (the overflow redo of
-    the lazy max), for <q, u> < 0 they fall far below it (underflow). Inside
-    each half the attention stays as diffuse as with plain N(0, 1) data."""
-    def prep(w, lay, raw):
-        k = workloads.as_f32(w, raw["k"]).copy()
-        u = np.random.default_rng(99).standard_normal(w.d).astype(np.float32)
-        u /= np.linalg.norm(u)
-        for s_ in range(w.C):
-            ls = pack.zigzag_layout(w.seqlens, w.C, s_)
-            late = ls["pos"] >= (ls["L"][ls["seq"]] + 1) // 2
-            k[s_][late] += lam * u
-        raw["k"] = workloads.f32_to_bf16_bits(k) if w.dtype == "bf16" else k
-    return prep
-
-
 def test_running_max_far_from_first_block(env):
     """Scores jumping about +-100 (log2 units) away from the first key block's:
     exercises the overflow redo of the forward's lazy running max and the
-    underflow of blocks far below it. Forward only: the backward uses the
-    final LSE and has no running max, and with a key component this large dQ
-    is dominated by the cancellation of sum_k dS (which is zero per row) times
-    that component, below what bf16 dS can resolve in any implementation."""
+    underflow of blocks far below it. The forward is checked here; the
+    backward at this shift is outside its input domain (next tests)."""
     w = _edge("maxjump", [1999, 700], 2, 1, pack.KIND_TTT, 2, 8, 2)
-    got, ref, _ = _run(env, w, with_bwd=False, prep=_shift_late_keys(600.0))
+    got, ref, _ = _run(env, w, with_bwd=False, prep=shift_late_keys(600.0))
     _check_fwd(w, got, ref)
+
+
+def test_backward_with_keys_sharing_a_50_unit_component(env):
+    """Late keys shifted by 50 u (scores move by about +-4 natural-log units
+    together): the whole backward stays inside its tolerance."""
+    w = _edge("maxjump", [1999, 700], 2, 1, pack.KIND_TTT, 2, 8, 2)
+    got, ref, _ = _run(env, w, with_bwd=True, prep=shift_late_keys(50.0))
+    _check_fwd(w, got, ref)
+    _check_bwd(w, got, ref)
+
+
+@pytest.mark.skip(reason="outside the bf16 backward's input domain: with late keys shifted by "
+                  "600 u, dQ measured max-abs 0.573 (0.465 allowed) and rel-L2 0.052 (1e-2 "
+                  "allowed); O and LSE pass. The CPU model in test_bf16_backward_model.py "
+                  "reproduces these numbers from three bf16 roundings (O before Delta, P in "
+                  "the forward's PV, dS before dS K), each of which alone exceeds the bound")
+def test_backward_with_keys_sharing_a_600_unit_component(env):
+    w = _edge("maxjump", [1999, 700], 2, 1, pack.KIND_TTT, 2, 8, 2)
+    got, ref, _ = _run(env, w, with_bwd=True, prep=shift_late_keys(600.0))
+    _check_fwd(w, got, ref)
+    _check_bwd(w, got, ref)
 
 
 def test_forward_is_deterministic_and_stream_ordered(env):
@@ -386,25 +386,27 @@ def test_graph_capture_replays_match_eager(env):
 # gradient sum rules that hold at any size
 
 
-def _sample_rows(lay, br, rng, n_main, n_anchor):
-    """First and last two rows of both local chunks of the first and last
-    sequence, plus seeded random rows; all branch rows of the first, the last
-    and a few random local anchors."""
+def _sample_rows(lay, br, rng, n_main, n_anchor, edge=64):
+    """The first and last ``edge`` rows of every local chunk of every
+    sequence, plus ``n_main`` seeded random rows; as anchors, every local
+    anchor on a sampled row, the first and the last, and ``n_anchor`` random
+    ones (all of an anchor's branch rows are taken)."""
     rows = set()
-    S = lay["L"].size
-    for s in sorted({0, S - 1}):
+    for s in range(lay["L"].size):
         c = int(lay["c"][s])
         for half in range(2):
             lo = int(lay["cu_local"][s]) + half * c
-            rows |= {lo, lo + min(1, c - 1), lo + c - 1, lo + max(c - 2, 0)}
+            rows |= set(range(lo, lo + min(edge, c)))
+            rows |= set(range(lo + max(c - edge, 0), lo + c))
     rows |= set(rng.choice(lay["n_local"], size=n_main, replace=False).tolist())
+    rows = np.array(sorted(rows), np.int64)
     A = br["anchor_row"].size
-    brows = []
+    anch = set()
     if A:
-        pick = {0, A - 1} | set(rng.choice(A, size=min(n_anchor, A), replace=False).tolist())
-        for a in sorted(pick):
-            brows += list(range(int(br["branch_off"][a]), int(br["branch_off"][a + 1])))
-    return sorted(rows), brows
+        on_row = np.isin(br["anchor_row"], rows)
+        anch = set(np.nonzero(on_row)[0].tolist()) | {0, A - 1}
+        anch |= set(rng.choice(A, size=min(n_anchor, A), replace=False).tolist())
+    return rows, np.array(sorted(anch), np.int64)
 
 
 class _DeviceRows:
@@ -484,6 +486,11 @@ def test_element_offsets_beyond_2_31(env):
 
 @pytest.mark.parametrize("name", ["ttt32k", "dflash", "dspark", "long256k"])
 def test_full_size_sampled(env, name):
+    """Full-size workloads: the first and last 64 rows of every local chunk
+    (and random rows and anchors) against the oracle's dense form of that row
+    subset; dK/dV element by element on every key whose viewers are all in the
+    subset (at long256k: the last 64 keys of the sequence); the gradient sum
+    rules over the whole tensors."""
     torch, ba = env
     w = workloads.make(name)
     say(f"[case] full-size {name}")
@@ -500,21 +507,18 @@ def test_full_size_sampled(env, name):
     torch.cuda.synchronize()
     say("  device pass done")
     rng = np.random.default_rng(7)
-    rows, brows = _sample_rows(lay, br, rng, n_main=12, n_anchor=3)
+    rows, anch = _sample_rows(lay, br, rng, n_main=12, n_anchor=3)
     L = {k: LazyF32(w, v) for k, v in raw.items()}
-    ref = attn.attn_rows(lay, br, L["q"], L["k"], L["v"], L["qb"], L["kb"], L["vb"], rows, brows,
-                         dtype=np.float32, do=L["do"] if w.bwd else None,
-                         dob=L["dob"] if w.bwd else None)
-    say(f"  oracle rows done ({len(rows)} main, {len(brows)} branch)")
+    t0 = time.time()
+    ref = subset_grouped(lay, br, L["q"], L["k"], L["v"], L["qb"], L["kb"], L["vb"], rows, anch,
+                         do=L["do"] if w.bwd else None, dob=L["dob"] if w.bwd else None)
+    brows = ref["branch_rows"]
+    say(f"  oracle rows done ({rows.size} main, {brows.size} branch) in {time.time() - t0:.0f} s")
     ri = torch.tensor(rows, device="cuda")
     bi = torch.tensor(brows, device="cuda", dtype=torch.long)
-    g_o, g_l = to_host(o[ri]), to_host(lse[ri])
-    w_o = np.stack([ref["main"][r]["o"] for r in rows])
-    w_l = np.stack([ref["main"][r]["lse"] for r in rows])
-    checks = [("o", g_o, w_o, g_l, w_l)]
-    if brows:
-        checks.append(("ob", to_host(ob[bi]), np.stack([ref["branch"][r]["o"] for r in brows]),
-                       to_host(lseb[bi]), np.stack([ref["branch"][r]["lse"] for r in brows])))
+    checks = [("o", to_host(o[ri]), ref["o"], to_host(lse[ri]), ref["lse"])]
+    if brows.size:
+        checks.append(("ob", to_host(ob[bi]), ref["ob"], to_host(lseb[bi]), ref["lseb"]))
     for nm, go, wo, gl, wl in checks:
         e_o, r_o, e_l = max_abs(go, wo), rel_l2(go, wo), lse_err(gl, wl)
         say(f"  {nm}: max|dO|={e_o:.3e} relL2={r_o:.3e} max|dLSE|={e_l:.3e}")
@@ -522,15 +526,23 @@ def test_full_size_sampled(env, name):
     if grads is None:
         return
     dq, dk, dv, dqb, dkb, dvb = grads
-    gq = to_host(dq[ri])
-    wq = np.stack([ref["main"][r]["dq"] for r in rows])
-    ok, ma, rl = grad_ok(gq, wq, True)
-    say(f"  dq: max-abs={ma:.3e} relL2={rl:.3e}")
-    assert ok
-    if brows:
-        ok, ma, rl = grad_ok(to_host(dqb[bi]), np.stack([ref["branch"][r]["dq"] for r in brows]), True)
-        say(f"  dqb: max-abs={ma:.3e} relL2={rl:.3e}")
-        assert ok
+    gchecks = [("dq", to_host(dq[ri]), ref["dq"])]
+    if brows.size:
+        gchecks.append(("dqb", to_host(dqb[bi]), ref["dqb"]))
+    keys, bkeys = complete_keys(lay, br, rows, anch)
+    kk = torch.tensor(keys, device="cuda")
+    gchecks += [("dk (complete keys)", to_host(dk[kk]), ref["dk"][keys]),
+                ("dv (complete keys)", to_host(dv[kk]), ref["dv"][keys])]
+    if bkeys.any():
+        bk = torch.tensor(bkeys, device="cuda")
+        gchecks += [("dkb (complete keys)", to_host(dkb[bk]), ref["dkb"][bkeys]),
+                    ("dvb (complete keys)", to_host(dvb[bk]), ref["dvb"][bkeys])]
+    say(f"  complete keys: {int(keys.sum())} main, {int(bkeys.sum())} branch")
+    assert keys.sum() >= 64
+    for nm, got, want in gchecks:
+        ok, ma, rl = grad_ok(got, want, True)
+        say(f"  {nm}: max-abs={ma:.3e} relL2={rl:.3e}")
+        assert ok, (nm, ma, rl)
     # sum rules per kv-group: sum_k dV_k = sum_q dO_q (real rows), sum_k dK_k = 0
     G = w.hq // w.hkv
     real = torch.tensor(lay["is_pad"] == 0, device="cuda")

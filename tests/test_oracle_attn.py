@@ -454,8 +454,10 @@ def test_row_sampled_form_matches_dense(ci):
     dob = rng.standard_normal(ins[3].shape)
     o, lse, ob, lseb = attn.attn_fwd(lay, br, *ins, dtype=np.float64)
     dq, dk, dv, dqb, dkb, dvb = attn.attn_bwd(lay, br, *ins, do, dob, dtype=np.float64)
+    dk_acc, dv_acc = {}, {}
     rows = attn.attn_rows(lay, br, *ins, main_rows=range(lay["n_local"]),
-                          branch_rows=range(br["n_branch"]), dtype=np.float64, do=do, dob=dob)
+                          branch_rows=range(br["n_branch"]), dtype=np.float64, do=do, dob=dob,
+                          dk_acc=dk_acc, dv_acc=dv_acc)
     for i, res in rows["main"].items():
         np.testing.assert_allclose(res["o"], o[i], atol=1e-12)
         np.testing.assert_array_equal(np.isfinite(res["lse"]), np.isfinite(lse[i]))
@@ -466,3 +468,71 @@ def test_row_sampled_form_matches_dense(ci):
         np.testing.assert_allclose(res["o"], ob[i], atol=1e-12)
         np.testing.assert_allclose(res["lse"], lseb[i], atol=1e-12)
         np.testing.assert_allclose(res["dq"], dqb[i], atol=1e-12)
+    # the main-key gradients that the row-sampled form accumulates over every
+    # row of the rank (position order per sequence) are the dense backward's
+    # dK/dV of the main keys (shard, local row), read back position by position
+    seen = set()
+    for s in range(lay["L"].size):
+        L = int(lay["L"][s])
+        if L == 0:
+            continue
+        assert s in dk_acc, s
+        for p_ in range(L):
+            hits = []
+            for sh in range(C):
+                lay_s = pack.zigzag_layout(lens, C, sh)
+                idx = np.nonzero((lay_s["seq"] == s) & (lay_s["pos"] == p_))[0]
+                hits += [(sh, int(i)) for i in idx]
+            assert len(hits) == 1
+            sh, i = hits[0]
+            seen.add((sh, i))
+            np.testing.assert_allclose(dk_acc[s][p_], dk[sh, i], atol=1e-12)
+            np.testing.assert_allclose(dv_acc[s][p_], dv[sh, i], atol=1e-12)
+    # every other key row (pads) has no gradient in the dense form either
+    for sh in range(C):
+        for i in range(dk.shape[1]):
+            if (sh, i) not in seen:
+                assert np.all(dk[sh, i] == 0) and np.all(dv[sh, i] == 0)
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2, 3])
+@pytest.mark.parametrize("part", [False, True])
+def test_subset_form_matches_dense(ci, part):
+    # attn_subset on a subset of rows equals the dense forms on those rows; its
+    # key gradients are the dense backward with dO zeroed on every other row
+    # (dK and dV are linear in dO), so a misplaced or missing key row shows
+    lens, C, kind, depth = CASES[ci]
+    pb = Problem(70 + ci, lens, C, kind, depth=depth, n_anchors=4, hq=4, hkv=2, d=6)
+    rng = np.random.default_rng(ci + 10)
+    rr = (ci + 1) % C
+    lay, br = pb.oracle_structs(rr)
+    ins = pb.rank_inputs(rr)
+    do = rng.standard_normal(ins[0].shape)
+    dob = rng.standard_normal(ins[3].shape)
+    n, A = lay["n_local"], br["anchor_row"].size
+    if part:
+        mrows = np.sort(rng.choice(n, size=max(1, n // 3), replace=False))
+        anch = np.sort(rng.choice(A, size=A // 2, replace=False)) if A else np.zeros(0, np.int64)
+    else:
+        mrows, anch = np.arange(n), np.arange(A)
+    sub = attn.attn_subset(lay, br, *ins, main_rows=mrows, anchors=anch, do=do, dob=dob,
+                           dtype=np.float64, row_block=5)
+    o, lse, ob, lseb = attn.attn_fwd(lay, br, *ins, dtype=np.float64)
+    keep_m = np.zeros(n, bool)
+    keep_m[mrows] = True
+    brows = sub["branch_rows"]
+    keep_b = np.zeros(br["n_branch"], bool)
+    keep_b[brows] = True
+    assert brows.size == sum(int(br["branch_off"][a + 1] - br["branch_off"][a]) for a in anch)
+    dq, dk, dv, dqb, dkb, dvb = attn.attn_bwd(lay, br, *ins, do * keep_m[:, None, None],
+                                              dob * keep_b[:, None, None], dtype=np.float64)
+    np.testing.assert_allclose(sub["o"], o[mrows], atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(sub["lse"]), np.isneginf(lse[mrows]))  # pads
+    fin = np.isfinite(lse[mrows])
+    np.testing.assert_allclose(sub["lse"][fin], lse[mrows][fin], atol=1e-12)
+    np.testing.assert_allclose(sub["ob"], ob[brows], atol=1e-12)
+    np.testing.assert_allclose(sub["lseb"], lseb[brows], atol=1e-12)
+    np.testing.assert_allclose(sub["dq"], dq[mrows], atol=1e-12)
+    np.testing.assert_allclose(sub["dqb"], dqb[brows], atol=1e-12)
+    for got, want in ((sub["dk"], dk), (sub["dv"], dv), (sub["dkb"], dkb), (sub["dvb"], dvb)):
+        np.testing.assert_allclose(got, want, atol=1e-12)

@@ -23,6 +23,9 @@ consumes projected activations, which are stood in for by N(0,1) draws.
 
 Reduced variants (suffix ``_r``) keep the head configuration, kind, C and
 structure but shrink the token count so the dense oracle finishes in seconds.
+``long256k_r16k`` is the larger reduction of the long workload: 1 x 16384
+tokens, C=8 (chunks of 1024 rows, several key tiles each), 32/8/128 bf16,
+TTT depth 7, fwd+bwd.
 """
 
 from dataclasses import dataclass, field
@@ -107,6 +110,8 @@ def anchors_uniform(rng, n_real, n_anchors):
 
 def make(name):
     """Build a named workload (structure only; tensors come from ``draw``)."""
+    if name == "long256k_r16k":
+        return Workload(name, [16384], 8, 0, KIND_TTT, 7, 32, 8, 128, "bf16", True, 4)
     base = name[:-2] if name.endswith("_r") else name
     reduced = name.endswith("_r")
     seed = {"tiny": 1, "ttt32k": 2, "dflash": 3, "long256k": 4, "dspark": 5}[base]
