@@ -97,6 +97,9 @@ def lib():
         L.ba_plan_destroy.argtypes = [ctypes.c_void_p]
         L.branch_attn_fwd.restype = ctypes.c_int
         L.branch_attn_fwd.argtypes = [ctypes.c_void_p, ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+        L.branch_attn_fwd_static.restype = ctypes.c_int
+        L.branch_attn_fwd_static.argtypes = [ctypes.c_void_p, ctypes.POINTER(FwdArgs),
+                                             ctypes.c_void_p]
         L.branch_attn_bwd.restype = ctypes.c_int
         L.branch_attn_bwd.argtypes = [ctypes.c_void_p, ctypes.POINTER(BwdArgs), ctypes.c_void_p]
         L.ba_plan_get_worklist.restype = ctypes.c_int
@@ -289,6 +292,44 @@ def fwd(plan, q, k, v, qb=None, kb=None, vb=None, scale=0.0, workspace=None):
         stream = torch.cuda.current_stream(dev).cuda_stream
         _check(lib().branch_attn_fwd(plan.handle, ctypes.byref(a), ctypes.c_void_p(stream)),
                "branch_attn_fwd")
+    return o, lse, ob, lseb
+
+
+def fwd_static(plan, q, k, v, qb=None, kb=None, vb=None, out=None, scale=0.0):
+    """Forward through ``branch_attn_fwd_static``: no workspace, so nothing is
+    allocated when the outputs are given as ``out = (o, lse, ob, lseb)``
+    (ob/lseb None without branch rows); otherwise they are allocated here.
+    Returns (o, lse, ob, lseb)."""
+    torch = _torch()
+    dev = q.device
+    dt = _tdtype(plan)
+    S = _shapes(plan)
+    nb = plan.info["n_branch_rows"]
+    _expect("q", q, S["q"], dt, dev)
+    _expect("k", k, S["k"], dt, dev)
+    _expect("v", v, S["k"], dt, dev)
+    if nb:
+        _expect("qb", qb, S["qb"], dt, dev)
+        _expect("kb", kb, S["kb"], dt, dev)
+        _expect("vb", vb, S["kb"], dt, dev)
+    if out is None:
+        out = (torch.empty(S["q"], dtype=dt, device=dev),
+               torch.empty(S["lse"], dtype=torch.float32, device=dev),
+               torch.empty(S["qb"], dtype=dt, device=dev) if nb else None,
+               torch.empty(S["lseb"], dtype=torch.float32, device=dev) if nb else None)
+    o, lse, ob, lseb = out
+    _expect("o", o, S["q"], dt, dev)
+    _expect("lse", lse, S["lse"], torch.float32, dev)
+    if nb:
+        _expect("ob", ob, S["qb"], dt, dev)
+        _expect("lseb", lseb, S["lseb"], torch.float32, dev)
+    a = FwdArgs(scale=float(scale), q=_ptr(q), k=_ptr(k), v=_ptr(v), qb=_ptr(qb), kb=_ptr(kb),
+                vb=_ptr(vb), o=_ptr(o), lse=_ptr(lse), ob=_ptr(ob), lseb=_ptr(lseb),
+                workspace=None, workspace_bytes=0)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _check(lib().branch_attn_fwd_static(plan.handle, ctypes.byref(a), ctypes.c_void_p(stream)),
+               "branch_attn_fwd_static")
     return o, lse, ob, lseb
 
 

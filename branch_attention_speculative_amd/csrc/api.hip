@@ -72,6 +72,45 @@ ba_status check_plan(const ba_plan *p) {
   return BA_OK;
 }
 
+// ---- static scratch of the no-allocation forward ---------------------------
+// Device memory of branch_attn_fwd_static: the forward's workspace (the fp32
+// main-key partial and its LSE of every branch row) lives in this array
+// instead of a caller buffer. Every GPU the library runs on holds its own
+// copy for the life of the process. Host code never uses the array's name as
+// an address: its device address is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_ptrs().
+constexpr size_t kStaticScratchBytes = size_t(256) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+struct ScratchPtrs {
+  std::mutex mu;
+  std::vector<void *> ptr;  // per device ordinal; nullptr until looked up
+};
+ScratchPtrs &scratch_ptrs() {
+  static ScratchPtrs *s = new ScratchPtrs();  // never destroyed: safe at process exit
+  return *s;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call for that device.
+ba_status scratch_on_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BA_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  ScratchPtrs &S = scratch_ptrs();
+  std::lock_guard<std::mutex> g(S.mu);
+  if (S.ptr.size() <= size_t(dev)) S.ptr.resize(size_t(dev) + 1, nullptr);
+  if (S.ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(BA_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    S.ptr[dev] = ptr;
+  }
+  *out = S.ptr[dev];
+  return BA_OK;
+}
+
 float resolve_scale(float s, int d) { return s > 0.f ? s : 1.0f / std::sqrt(float(d)); }
 
 ba::F32Shape f32_shape(const ba_plan &p, float scale) {
@@ -108,6 +147,10 @@ extern "C" ba_status ba_plan_upload(ba_plan *p) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    // set-up of this device for the no-allocation forward as well
+    void *scr = nullptr;
+    ba_status st = scratch_on_current_device(&scr);
+    if (st != BA_OK) return st;
     if (p->dev.block != nullptr) {
       if (dev == p->dev.device) return BA_OK;
       return fail(BA_E_INVALID, "plan already uploaded to device " + std::to_string(p->dev.device));
@@ -175,20 +218,60 @@ extern "C" void ba_plan_destroy(ba_plan *p) {
   delete p;
 }
 
+namespace {
+
+// The forward with its workspace given explicitly (the caller's buffer, or
+// the static scratch); the plan has been checked.
+ba_status fwd_impl(const ba_plan *p, const ba_fwd_args *a, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+}  // namespace
+
 extern "C" ba_status branch_attn_fwd(const ba_plan *p, const ba_fwd_args *a, void *stream) {
   try {
     ba_status st = check_plan(p);
     if (st != BA_OK) return st;
     if (a == nullptr) return fail(BA_E_INVALID, "args is NULL");
+    return fwd_impl(p, a, a->workspace, a->workspace_bytes, stream);
+  } catch (...) {
+    return fail(BA_E_INVALID, "unexpected error in branch_attn_fwd");
+  }
+}
+
+extern "C" ba_status branch_attn_fwd_static(const ba_plan *p, const ba_fwd_args *a, void *stream) {
+  try {
+    ba_status st = check_plan(p);
+    if (st != BA_OK) return st;
+    if (p->ws_fwd > kStaticScratchBytes)
+      return fail(BA_E_WORKSPACE, "the plan's forward workspace (" + std::to_string(p->ws_fwd) +
+                                      " bytes) exceeds the static scratch (" +
+                                      std::to_string(kStaticScratchBytes) + " bytes)");
+    if (a == nullptr) return fail(BA_E_INVALID, "args is NULL");
+    if (a->workspace != nullptr || a->workspace_bytes != 0)
+      return fail(BA_E_INVALID, "branch_attn_fwd_static takes no workspace (pass NULL and 0)");
+    void *scr = nullptr;
+    st = scratch_on_current_device(&scr);
+    if (st != BA_OK) return st;
+    return fwd_impl(p, a, scr, kStaticScratchBytes, stream);
+  } catch (...) {
+    return fail(BA_E_INVALID, "unexpected error in branch_attn_fwd_static");
+  }
+}
+
+namespace {
+
+ba_status fwd_impl(const ba_plan *p, const ba_fwd_args *a, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+  try {
     if (!a->q || !a->k || !a->v || !a->o || !a->lse)
       return fail(BA_E_INVALID, "q, k, v, o and lse are required");
     const bool has_b = p->n_branch > 0;
     if (has_b && (!a->qb || !a->kb || !a->vb || !a->ob || !a->lseb))
       return fail(BA_E_INVALID, "qb, kb, vb, ob and lseb are required when the plan has branch rows");
     for (const void *ptr : {a->q, a->k, a->v, (const void *)a->o, (const void *)a->lse, a->qb, a->kb,
-                            a->vb, (const void *)a->ob, (const void *)a->lseb, (const void *)a->workspace})
+                            a->vb, (const void *)a->ob, (const void *)a->lseb, (const void *)workspace})
       if (!aligned16(ptr)) return fail(BA_E_INVALID, "every pointer must be 16-byte aligned");
-    if (p->ws_fwd > 0 && (a->workspace == nullptr || a->workspace_bytes < p->ws_fwd))
+    if (p->ws_fwd > 0 && (workspace == nullptr || workspace_bytes < p->ws_fwd))
       return fail(BA_E_WORKSPACE, "forward workspace needs " + std::to_string(p->ws_fwd) + " bytes");
     if (!(std::isfinite(a->scale))) return fail(BA_E_INVALID, "scale must be finite");
     const float scale = resolve_scale(a->scale, p->d);
@@ -196,9 +279,9 @@ extern "C" ba_status branch_attn_fwd(const ba_plan *p, const ba_fwd_args *a, voi
 
     float *om = nullptr, *lm = nullptr;
     if (has_b) {
-      om = static_cast<float *>(a->workspace);
+      om = static_cast<float *>(workspace);
       const size_t om_bytes = (size_t(p->n_branch) * p->hq * p->d * 4 + 255) & ~size_t(255);
-      lm = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + om_bytes);
+      lm = reinterpret_cast<float *>(static_cast<char *>(workspace) + om_bytes);
     }
     ba::FwdRingArgs ra{};
     ra.q = a->q;
@@ -256,9 +339,11 @@ extern "C" ba_status branch_attn_fwd(const ba_plan *p, const ba_fwd_args *a, voi
     }
     return BA_OK;
   } catch (...) {
-    return fail(BA_E_INVALID, "unexpected error in branch_attn_fwd");
+    return fail(BA_E_INVALID, "unexpected error in the forward");
   }
 }
+
+}  // namespace
 
 extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, void *stream) {
   try {

@@ -200,6 +200,26 @@ typedef struct {
 ba_status branch_attn_fwd(const ba_plan *plan, const ba_fwd_args *args, void *stream);
 
 /*
+ * The forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same kernels and results as branch_attn_fwd,
+ * with the workspace taken from a static device array of the library
+ * (256 MiB, one copy per GPU, held until the process ends; its address is
+ * looked up once per device by ba_plan_upload). It allocates nothing and
+ * synchronises nothing.
+ *   args->workspace must be NULL and args->workspace_bytes 0 (BA_E_INVALID
+ *   otherwise); every other field as for branch_attn_fwd.
+ *   Plans whose ws_fwd_bytes exceeds 256 MiB are rejected with BA_E_WORKSPACE
+ *   before any argument is read or any kernel is enqueued.
+ *   The array needs no clearing: every byte a call reads was written earlier
+ *   in the same call.
+ *   All calls on one GPU share the array: calls whose kernels can overlap
+ *   (different streams without ordering between them) race on it and give
+ *   undefined results. Calls on one stream, or ordered by events, are safe.
+ */
+ba_status branch_attn_fwd_static(const ba_plan *plan, const ba_fwd_args *args, void *stream);
+
+/*
  * Backward, recomputed from the merged LSE: Delta = rowsum(dO * O), then the
  * ring replay (dQ for every local row; dK/dV for every shard), the branch-local
  * backward, and the final sums. Enqueue only.
