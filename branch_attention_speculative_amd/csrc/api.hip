@@ -65,10 +65,16 @@ ba_status hip_fail(const char *what, hipError_t e) {
 
 ba_status check_plan(const ba_plan *p) {
   if (p == nullptr) return fail(BA_E_INVALID, "plan is NULL");
-  if (p->dev.block == nullptr) return fail(BA_E_INVALID, "plan not uploaded (call ba_plan_upload)");
+  int uploaded_to = -1;
+  {
+    std::lock_guard<std::mutex> g(p->dev_mu);
+    if (p->dev.block == nullptr)
+      return fail(BA_E_INVALID, "plan not uploaded (call ba_plan_upload)");
+    uploaded_to = p->dev.device;
+  }
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(BA_E_HIP, "hipGetDevice failed");
-  if (dev != p->dev.device) return fail(BA_E_INVALID, "plan was uploaded to another device");
+  if (dev != uploaded_to) return fail(BA_E_INVALID, "plan was uploaded to another device");
   return BA_OK;
 }
 
@@ -144,6 +150,7 @@ ba::F32Shape f32_shape(const ba_plan &p, float scale) {
 extern "C" ba_status ba_plan_upload(ba_plan *p) {
   try {
     if (p == nullptr) return fail(BA_E_INVALID, "plan is NULL");
+    std::lock_guard<std::mutex> guard(p->dev_mu);
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);

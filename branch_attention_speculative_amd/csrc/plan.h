@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -89,6 +90,9 @@ struct ba_plan {
   int64_t pairs_main = 0, pairs_prefix = 0, pairs_local = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
   ba::DevPlan dev;
+  // guards dev: ba_plan_upload may run on several threads at once, and
+  // fwd/bwd read dev under it
+  mutable std::mutex dev_mu;
 };
 
 namespace ba {

@@ -47,8 +47,9 @@
  * Ownership and threading:
  *   - The caller owns every device buffer and the stream. A plan is created
  *     on the host (ba_plan_create), uploaded once to the current device
- *     (ba_plan_upload: the only call that allocates device memory), and is
- *     immutable afterwards, so concurrent use on several streams is safe.
+ *     (ba_plan_upload: the only call that allocates device memory; it may be
+ *     called from several threads at once), and is immutable afterwards, so
+ *     concurrent use on several streams is safe.
  *   - branch_attn_fwd / branch_attn_bwd never allocate and never synchronise:
  *     they validate, then enqueue kernels on the caller's stream and return.
  *     Asynchronous device faults surface at the caller's next synchronisation.
