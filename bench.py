@@ -32,8 +32,13 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096)
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 matrix-core peak (256 CU x 2.4 GHz x 8192)
+# the fp8 forward does half its FLOPs (Q K^T) at the fp8 rate, half (P V) at the bf16 rate
+PEAK_FP8_QK_BF16_PV_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 METRIC = "branch-attn fwd+bwd effective TFLOP/s (1 GPU) and % of bf16 MFMA peak"
+METRIC_FP8 = ("branch-attn fwd effective TFLOP/s (1 GPU), fp8 E4M3 Q K^T with bf16 P V, and % of "
+              "the matching fp8/bf16 MFMA peak")
 
 # algorithmic FLOP per unmasked pair per q-head and per unit of D, per kernel:
 # the forward ring kernel does Q K^T and P V over the main keys; the dK/dV
@@ -49,9 +54,11 @@ KERNEL_SOURCES = {"fwd_ring": ["fwd_ring.hip", "ring_common.h", "common.h"],
 def describe(w, info):
     kind = {0: "no branches", 1: f"EAGLE-3 TTT depth {w.depth_or_block}",
             2: "DFlash bidirectional blocks", 3: "DSpark causal blocks"}[w.kind]
+    dt = "fp8 E4M3 q/k, bf16 v/o" if w.dtype == "fp8" else w.dtype
+    passes = "fwd+bwd" if w.bwd else "fwd"
     return (f"{w.name}: {len(w.seqlens)} seq / {sum(w.seqlens)} tokens, virtual CP={w.C} rank {w.r} "
             f"share ({info['n_local_rows']} local rows, {info['n_branch_rows']} branch rows), "
-            f"{w.hq}/{w.hkv} heads, d={w.d}, {w.dtype}, {kind}, fwd+bwd")
+            f"{w.hq}/{w.hkv} heads, d={w.d}, {dt}, {kind}, {passes}")
 
 
 def source_hash(names):
@@ -74,6 +81,18 @@ def read_traffic(kernel, workload):
     if not (m_b and m_h) or m_h.group(1) != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return float(m_b.group(1))
+
+
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, plan_info, raw, n_anchor_sample, seed=11):
@@ -106,9 +125,13 @@ def cpu_baseline(w, plan_info, raw, n_anchor_sample, seed=11):
     L = {k: Lazy(v) for k, v in raw.items()}
     dk_acc, dv_acc = {}, {}
     t0 = time.perf_counter()
-    attn.attn_rows(lay, br, L["q"], L["k"], L["v"], L["qb"], L["kb"], L["vb"], main_rows,
-                   branch_rows, dtype=np.float32, do=L["do"], dob=L["dob"], dk_acc=dk_acc,
-                   dv_acc=dv_acc)
+    if w.bwd:
+        attn.attn_rows(lay, br, L["q"], L["k"], L["v"], L["qb"], L["kb"], L["vb"], main_rows,
+                       branch_rows, dtype=np.float32, do=L["do"], dob=L["dob"], dk_acc=dk_acc,
+                       dv_acc=dv_acc)
+    else:
+        attn.attn_rows(lay, br, L["q"], L["k"], L["v"], L["qb"], L["kb"], L["vb"], main_rows,
+                       branch_rows, dtype=np.float32)
     dt = time.perf_counter() - t0
     # unmasked pairs of the sampled rows, from the visibility rules
     pairs = int(np.sum(lay["pos"][main_rows] + 1))
@@ -117,13 +140,15 @@ def cpu_baseline(w, plan_info, raw, n_anchor_sample, seed=11):
         n = br["branch_off"][a + 1] - br["branch_off"][a]
         own = n if br["kind"] == pack.KIND_BLOCK_BIDIR else br["b_j"][b] + 1
         pairs += int(br["anchor_pos"][a]) + 1 + int(own)
-    flop = pairs * w.hq * w.d * 14
+    flop = pairs * w.hq * w.d * (14 if w.bwd else 4)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     total_pairs = plan_info["pairs_total"]
     return {
         "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{len(main_rows)} anchors of the same workload: their {len(main_rows)} main rows "
-                   f"+ {len(branch_rows)} branch rows x {w.hq} heads, fwd+bwd against full key sets "
+                   f"+ {len(branch_rows)} branch rows x {w.hq} heads, "
+                   f"{'fwd+bwd' if w.bwd else 'fwd'} against full key sets "
                    f"({pairs} of {total_pairs} pairs per head, {dt:.1f} s, fp32 NumPy)"),
         "seconds": dt, "extrapolated_step_s": dt * total_pairs / max(pairs, 1),
     }
@@ -146,6 +171,9 @@ def main():
                          "(0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="fp8: Q/K/Qb/Kb as fp8 E4M3, V bf16, forward only (a step is the "
+                         "forward; the metric and peak change accordingly)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -167,21 +195,25 @@ def main():
             print("--tokens applies to the long256k workload only", file=sys.stderr)
             sys.exit(2)
         w = dataclasses.replace(w, name=f"ttt{args.tokens}", seqlens=[args.tokens])
+    fp8 = args.dtype == "fp8"
+    if fp8:
+        w = dataclasses.replace(w, dtype="fp8", bwd=False)
     plan = ba.Plan(w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.anchors, w.branch_lens,
                    w.hq, w.hkv, w.d, w.dtype).upload()
     info = plan.info
     N, NB = info["n_local_rows"], info["n_branch_rows"]
     print(f"[bench] {describe(w, info)}", file=sys.stderr, flush=True)
-    raw = workloads.draw(w, N, NB)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    raw = workloads.draw(w, N, NB, names=workloads.TENSOR_ORDER if w.bwd else
+                         ["q", "k", "v", "qb", "kb", "vb"])
 
     def dev(a):
-        if w.dtype == "bf16":
+        if a.dtype == np.uint8:  # fp8 E4M3 codes
+            return torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
+        if a.dtype == np.uint16:  # bf16 bits
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
     T = {k: dev(v) for k, v in raw.items()}
-    del tdt
     ws_f = torch.empty(max(info["ws_fwd_bytes"], 1), dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(max(info["ws_bwd_bytes"], 1), dtype=torch.uint8, device="cuda")
     print("[bench] inputs resident", file=sys.stderr, flush=True)
@@ -189,6 +221,8 @@ def main():
     def step():
         o, lse, ob, lseb = ba.fwd(plan, T["q"], T["k"], T["v"], T["qb"], T["kb"], T["vb"],
                                   workspace=ws_f)
+        if not w.bwd:
+            return o, lse, ob, lseb
         return ba.bwd(plan, T["q"], T["k"], T["v"], T["qb"], T["kb"], T["vb"], o, lse, ob, lseb,
                       T["do"], T["dob"], workspace=ws_b)
 
@@ -225,8 +259,9 @@ def main():
 
     pairs = info["pairs_total"]
     pairs_main_keys = info["pairs_main"] + info["pairs_prefix"]
-    flop_step = pairs * w.hq * w.d * (4 + 10)
+    flop_step = pairs * w.hq * w.d * (4 + (10 if w.bwd else 0))
     tflops = flop_step / (ms * 1e-3) / 1e12
+    peak = PEAK_FP8_QK_BF16_PV_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     kernels = {}
     for name, (n, tot) in kern.items():
         avg = tot / max(n, 1)
@@ -241,9 +276,9 @@ def main():
         dom = max((k for k in kernels if k in KERNEL_FLOP_PER_PAIR_D),
                   key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
         ach = kernels[dom]["achieved_tflops"]
-        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                "traffic": read_traffic(dom, w.name)}
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak,
+                "unit": "TFLOP/s", "frac": ach / peak,
+                "traffic": None if fp8 else read_traffic(dom, w.name)}
     probe = None
     if args.mfma_probe_iters > 0:
         # what the matrix cores sustain on register operands on this part, zero
@@ -258,7 +293,7 @@ def main():
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, info, raw, args.cpu_anchors)
     out = {
-        "metric": METRIC,
+        "metric": METRIC_FP8 if fp8 else METRIC,
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -273,7 +308,7 @@ def main():
         "config": {"workload": describe(w, info), "tokens": int(sum(w.seqlens)),
                    "cp_degree": w.C, "cp_rank": w.r, "local_rows": N, "branch_rows": NB,
                    "pairs_per_head": pairs, "flop_per_step": flop_step},
-        "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "pct_of_peak": 100.0 * tflops / peak,
         "roofline": roof,
         "cpu_baseline": cpu,
         "mfma_probe": probe,
@@ -287,9 +322,9 @@ def main():
         bwd_ms = sum(k["avg_ms"] * k["launches_per_step"] for n, k in kernels.items()
                      if n.startswith("bwd"))
         f_fwd, f_bwd = pairs * w.hq * w.d * 4, pairs * w.hq * w.d * 10
-        out["split"] = {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        out["split"] = {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms if w.bwd else None,
                         "fwd_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,
-                        "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12 if bwd_ms else None}
+                        "bwd_tflops": f_bwd / (bwd_ms * 1e-3) / 1e12 if (bwd_ms and w.bwd) else None}
     print(json.dumps(out))
 
 

@@ -13,7 +13,9 @@ is no fallback: if the library is missing the calls raise.
 
 Tensor layouts are those of the header: q/o [N, hq, d]; k/v [C, N, hkv, d]
 (shard s = rank s's local rows); qb/ob [NB, hq, d]; kb/vb [NB, hkv, d];
-lse [N, hq], lseb [NB, hq] float32.
+lse [N, hq], lseb [NB, hq] float32. Element types: dtype "bf16" (bf16
+throughout), "fp32" (float32 throughout) or "fp8" (q, k, qb, kb as
+torch.float8_e4m3fn, i.e. OCP fp8 E4M3; v, vb, o, ob bf16; forward only).
 """
 
 import ctypes
@@ -22,7 +24,7 @@ import os
 import numpy as np
 
 KIND_NONE, KIND_TTT, KIND_BLOCK_BIDIR, KIND_BLOCK_CAUSAL = 0, 1, 2, 3
-DTYPES = {"bf16": 0, "fp32": 1}
+DTYPES = {"bf16": 0, "fp32": 1, "fp8": 2}
 
 BA_OK = 0
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -221,8 +223,15 @@ def _torch():
 
 
 def _tdtype(plan):
+    """Element type of v, vb, o, ob and of the gradients."""
     t = _torch()
-    return t.bfloat16 if plan.dtype == "bf16" else t.float32
+    return t.float32 if plan.dtype == "fp32" else t.bfloat16
+
+
+def _qkdtype(plan):
+    """Element type of q, k, qb, kb."""
+    t = _torch()
+    return t.float8_e4m3fn if plan.dtype == "fp8" else _tdtype(plan)
 
 
 def _ptr(t):
@@ -268,14 +277,15 @@ def fwd(plan, q, k, v, qb=None, kb=None, vb=None, scale=0.0, workspace=None):
     torch = _torch()
     dev = q.device
     dt = _tdtype(plan)
+    dq8 = _qkdtype(plan)
     S = _shapes(plan)
     nb = plan.info["n_branch_rows"]
-    _expect("q", q, S["q"], dt, dev)
-    _expect("k", k, S["k"], dt, dev)
+    _expect("q", q, S["q"], dq8, dev)
+    _expect("k", k, S["k"], dq8, dev)
     _expect("v", v, S["k"], dt, dev)
     if nb:
-        _expect("qb", qb, S["qb"], dt, dev)
-        _expect("kb", kb, S["kb"], dt, dev)
+        _expect("qb", qb, S["qb"], dq8, dev)
+        _expect("kb", kb, S["kb"], dq8, dev)
         _expect("vb", vb, S["kb"], dt, dev)
     o = torch.empty(S["q"], dtype=dt, device=dev)
     lse = torch.empty(S["lse"], dtype=torch.float32, device=dev)
@@ -303,14 +313,15 @@ def fwd_static(plan, q, k, v, qb=None, kb=None, vb=None, out=None, scale=0.0):
     torch = _torch()
     dev = q.device
     dt = _tdtype(plan)
+    dq8 = _qkdtype(plan)
     S = _shapes(plan)
     nb = plan.info["n_branch_rows"]
-    _expect("q", q, S["q"], dt, dev)
-    _expect("k", k, S["k"], dt, dev)
+    _expect("q", q, S["q"], dq8, dev)
+    _expect("k", k, S["k"], dq8, dev)
     _expect("v", v, S["k"], dt, dev)
     if nb:
-        _expect("qb", qb, S["qb"], dt, dev)
-        _expect("kb", kb, S["kb"], dt, dev)
+        _expect("qb", qb, S["qb"], dq8, dev)
+        _expect("kb", kb, S["kb"], dq8, dev)
         _expect("vb", vb, S["kb"], dt, dev)
     if out is None:
         out = (torch.empty(S["q"], dtype=dt, device=dev),

@@ -316,6 +316,8 @@ ba_status fwd_impl(const ba_plan *p, const ba_fwd_args *a, void *workspace, size
     hipError_t e;
     if (p->dtype == BA_BF16) {
       e = timed("fwd_ring", s, [&] { return ba::launch_fwd_ring_bf16(ra, int(p->qtiles.size()), s); });
+    } else if (p->dtype == BA_FP8) {
+      e = timed("fwd_ring", s, [&] { return ba::launch_fwd_ring_fp8(ra, int(p->qtiles.size()), s); });
     } else {
       const ba::F32Shape sh = f32_shape(*p, scale);
       e = timed("fwd_ring", s, [&] { return ba::launch_fwd_ring_f32(ra, sh, s); });
@@ -356,6 +358,8 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
   try {
     ba_status st = check_plan(p);
     if (st != BA_OK) return st;
+    if (p->dtype == BA_FP8)
+      return fail(BA_E_UNSUPPORTED, "the fp8 path is forward only (no backward for fp8 inputs)");
     if (a == nullptr) return fail(BA_E_INVALID, "args is NULL");
     if (!a->q || !a->k || !a->v || !a->o || !a->lse || !a->dout || !a->dq || !a->dk || !a->dv)
       return fail(BA_E_INVALID, "q, k, v, o, lse, dout, dq, dk and dv are required");

@@ -82,6 +82,21 @@ __device__ __forceinline__ void ld8_keep<float>(const float *p, int64_t i, float
   }
 }
 
+// fp8 E4M3 codes (Q and K of the fp8 path): 8 consecutive bytes, 8-byte aligned
+template <>
+__device__ __forceinline__ void ld8<uint8_t>(const uint8_t *p, int64_t i, float (&o)[8]) {
+  const u32x2 x = *reinterpret_cast<const u32x2 *>(p + i);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(x[k]), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(x[k]), true);
+    o[4 * k] = lo[0];
+    o[4 * k + 1] = lo[1];
+    o[4 * k + 2] = hi[0];
+    o[4 * k + 3] = hi[1];
+  }
+}
+
 // load 4 consecutive elements as floats (8-byte aligned for bf16, 16 for fp32)
 template <typename T>
 __device__ __forceinline__ void ld4(const T *p, int64_t i, float (&o)[4]);
@@ -115,34 +130,39 @@ __device__ __forceinline__ void st8<float>(float *p, int64_t i, const float (&v)
   *reinterpret_cast<f32x4 *>(p + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-// Stage the branch keys/values of a tile (rows [base, base + rows), kv-head g)
-// in LDS in the input type, row-major [row][DIM] (half the LDS of floats for
-// bf16, so that more workgroups fit on a compute unit).
+// Stage branch key or value rows of a tile (rows [base, base + rows), kv-head
+// g) in LDS in their input type, row-major [row][DIM] (half the LDS of floats
+// for bf16, a quarter for fp8, so that more workgroups fit on a compute unit).
 template <typename T, int DIM>
-__device__ __forceinline__ void stage_branch_kv(const T *KB, const T *VB, int base, int rows,
-                                                int g, int hkv, T *sK, T *sV) {
+__device__ __forceinline__ void stage_rows(const T *X, int base, int rows, int g, int hkv, T *sX) {
   constexpr int PER = 16 / sizeof(T);  // elements per 16-byte chunk
   for (int id = threadIdx.x; id < rows * (DIM / PER); id += blockDim.x) {
     const int rr = id / (DIM / PER), dc = id % (DIM / PER);
     const int64_t off = (int64_t(base + rr) * hkv + g) * DIM + dc * PER;
-    *reinterpret_cast<u32x4 *>(sK + rr * DIM + dc * PER) = *reinterpret_cast<const u32x4 *>(KB + off);
-    *reinterpret_cast<u32x4 *>(sV + rr * DIM + dc * PER) = *reinterpret_cast<const u32x4 *>(VB + off);
+    *reinterpret_cast<u32x4 *>(sX + rr * DIM + dc * PER) = *reinterpret_cast<const u32x4 *>(X + off);
   }
+}
+template <typename T, int DIM>
+__device__ __forceinline__ void stage_branch_kv(const T *KB, const T *VB, int base, int rows,
+                                                int g, int hkv, T *sK, T *sV) {
+  stage_rows<T, DIM>(KB, base, rows, g, hkv, sK);
+  stage_rows<T, DIM>(VB, base, rows, g, hkv, sV);
 }
 
 // ---------------------------------------------------------------------------
 
-template <typename T, int DIM, int MAXB>
+// TQ: element type of qb and kb; T: of vb and ob.
+template <typename TQ, typename T, int DIM, int MAXB>
 __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
-  __shared__ __attribute__((aligned(16))) T sK[kMaxBranch * DIM];
+  __shared__ __attribute__((aligned(16))) TQ sK[kMaxBranch * DIM];
   __shared__ __attribute__((aligned(16))) T sV[kMaxBranch * DIM];
   const BTile t = a.btiles[blockIdx.x];
   if (t.rows == 0) return;
   const int base = a.branch_off[t.a0];
   const int G = a.G;
-  const T *QB = static_cast<const T *>(a.qb);
-  stage_branch_kv<T, DIM>(static_cast<const T *>(a.kb), static_cast<const T *>(a.vb), base, t.rows,
-                          t.g, a.hkv, sK, sV);
+  const TQ *QB = static_cast<const TQ *>(a.qb);
+  stage_rows<TQ, DIM>(static_cast<const TQ *>(a.kb), base, t.rows, t.g, a.hkv, sK);
+  stage_rows<T, DIM>(static_cast<const T *>(a.vb), base, t.rows, t.g, a.hkv, sV);
   __syncthreads();
   // four threads per query vector, each over a quarter of D: contiguous
   // reads of q and of the partial, contiguous writes of the output
@@ -165,12 +185,12 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
     for (int dc = 0; dc < QD / 8; ++dc) {
       const int d0 = sub * QD + dc * 8;
       float q8[8];
-      ld8<T>(QB, qh * DIM + d0, q8);
+      ld8<TQ>(QB, qh * DIM + d0, q8);
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) {
         if (jj < nvis) {
           float kr[8];
-          ld8<T>(sK, (kl0 + jj) * DIM + d0, kr);
+          ld8<TQ>(sK, (kl0 + jj) * DIM + d0, kr);
           float acc = s[jj];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc = fmaf(q8[e], kr[e], acc);
@@ -438,16 +458,16 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
   }
 }
 
-template <typename T, int DIM>
+template <typename TQ, typename T, int DIM>
 hipError_t fwd_branch_dispatch(const FwdBranchArgs &a, int n, int maxb, hipStream_t s) {
   if (maxb <= 8)
-    hipLaunchKernelGGL((fwd_branch_kernel<T, DIM, 8>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_branch_kernel<TQ, T, DIM, 8>), dim3(n), dim3(256), 0, s, a);
   else if (maxb <= 16)
-    hipLaunchKernelGGL((fwd_branch_kernel<T, DIM, 16>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_branch_kernel<TQ, T, DIM, 16>), dim3(n), dim3(256), 0, s, a);
   else if (maxb <= 32)
-    hipLaunchKernelGGL((fwd_branch_kernel<T, DIM, 32>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_branch_kernel<TQ, T, DIM, 32>), dim3(n), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_branch_kernel<T, DIM, 64>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_branch_kernel<TQ, T, DIM, 64>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -469,9 +489,10 @@ hipError_t bwd_branch_dispatch(const BwdBranchArgs &a, int n, int maxb, hipStrea
 hipError_t launch_fwd_branch(const FwdBranchArgs &a, int n_tiles, int dtype, int maxb,
                              hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  if (dtype == BA_BF16) return fwd_branch_dispatch<u16, 128>(a, n_tiles, maxb, s);
-  if (a.d == 64) return fwd_branch_dispatch<float, 64>(a, n_tiles, maxb, s);
-  return fwd_branch_dispatch<float, 128>(a, n_tiles, maxb, s);
+  if (dtype == BA_BF16) return fwd_branch_dispatch<u16, u16, 128>(a, n_tiles, maxb, s);
+  if (dtype == BA_FP8) return fwd_branch_dispatch<uint8_t, u16, 128>(a, n_tiles, maxb, s);
+  if (a.d == 64) return fwd_branch_dispatch<float, float, 64>(a, n_tiles, maxb, s);
+  return fwd_branch_dispatch<float, float, 128>(a, n_tiles, maxb, s);
 }
 
 hipError_t launch_bwd_pre(const BwdPreArgs &a, int dtype, hipStream_t s) {

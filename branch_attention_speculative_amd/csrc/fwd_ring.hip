@@ -33,6 +33,14 @@
 // is computed (one barrier per block). Eight waves share each tile, which
 // halves the tile traffic into LDS per product compared with four.
 
+//
+// The fp8 instance (template flag QK8) takes Q and K as OCP fp8 E4M3 codes
+// and forms the scores with the gfx950 fp8 matrix-core product
+// (32x32x64, fp32 accumulate: two products per 32-key tile over D = 128
+// instead of eight bf16 ones); V, P, O and the softmax are the bf16
+// instance's. A K tile is then 64 rows of 128 bytes in LDS, swizzled by its
+// own rule (fp8 K tile layout below).
+
 #include "kernels.h"
 #include "ring_common.h"
 
@@ -43,11 +51,68 @@ namespace {
 constexpr int kBN = 64;  // keys per block
 constexpr float kOver = 18446744073709551616.f;  // 2^64: largest sum of P per lane and block
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 struct FwdState {
-  bf16x8 qreg[8];
+  bf16x8 qreg[8];  // bf16 instance: Q^T operands, 8 steps of 16 of D
+  i32x8 q8[2];     // fp8 instance: Q^T operands, 2 steps of 64 of D
   f32x16 acc[4];
   float mrun, lsum;
 };
+
+// ---- fp8 K tile layout ------------------------------------------------------
+// 64 key rows x 128 fp8 bytes, no padding; logical 16-byte chunk c of row r
+// sits at physical chunk c ^ swz8(r), swz8(r) = (r >> 1) & 7. Rows are 128
+// bytes (half the 256-byte bank sweep), so the 16 lanes of a quarter wave
+// that read one chunk of 16 consecutive rows hit bank groups
+// 8 (r & 1) + (c ^ swz8(r)): the even rows fill groups 0..7 and the odd rows
+// 8..15, each exactly once.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+// 32x32x64 fp8 (E4M3) x fp8 matrix-core product, fp32 accumulate. Operand
+// lane layout (lane l, i = l % 32, h = l / 32): A (32 x 64): A[i][32h .. 32h+31];
+// B (64 x 32): B[32h .. 32h+31][i]; C as for mfma32.
+__device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Byte offsets of this lane's two 16-byte reads of the A operand for key
+// rows 0..31 and D step kk (bytes 64 kk + 32 h .. + 31): add 32 * 128 for
+// key rows 32..63.
+struct Nat8Off {
+  int o[2][2];
+};
+__device__ __forceinline__ Nat8Off nat8_offsets(int lane) {
+  const int i = lane & 31, h = lane >> 5;
+  Nat8Off r;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) r.o[kk][t] = 128 * i + 16 * ((4 * kk + 2 * h + t) ^ swz8(i));
+  return r;
+}
+__device__ __forceinline__ i32x8 lds_nat8(const u16 *X, int row0, int kk, const Nat8Off &no) {
+  const char *b = reinterpret_cast<const char *>(X) + 128 * row0;
+  const u32x4 lo = *reinterpret_cast<const u32x4 *>(b + no.o[kk][0]);
+  const u32x4 hi = *reinterpret_cast<const u32x4 *>(b + no.o[kk][1]);
+  return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+               int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+}
+
+// Direct global -> LDS load of a 64-row fp8 K tile: 8 KB, one 1 KB
+// instruction per wave of the 8. Instruction J fills rows 8J .. 8J + 7; its
+// lane i writes physical chunk i % 8 of row 8J + i / 8, i.e. logical chunk
+// (i % 8) ^ swz8(row). rowstride: bytes between key rows in global memory.
+__device__ __forceinline__ uint32_t dma8_offset(int wave, int lane, int64_t rowstride) {
+  const int row = 8 * wave + (lane >> 3);
+  const int c = (lane & 7) ^ swz8(row);
+  return uint32_t(int64_t(row) * rowstride + 16 * c);
+}
+__device__ __forceinline__ void dma_tile64_f8(u16 *lds_tile, __amdgpu_buffer_rsrc_t rs,
+                                              uint32_t off, int wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(reinterpret_cast<char *>(lds_tile) + 1024 * wave),
+                                           16, off, 0, 0, 0);
+}
 
 // Block of the ring walk: segment sg (with its chunk info) and first key j0
 // inside the chunk.
@@ -78,6 +143,18 @@ __device__ __forceinline__ void scores(Scores &x, const u16 *bk, const FwdState 
   for (int ks = 0; ks < 8; ++ks) {
     x[0] = mfma32(lds_nat_o(bk, 0, ks, no), st.qreg[ks], x[0]);
     x[1] = mfma32(lds_nat_o(bk, 32, ks, no), st.qreg[ks], x[1]);
+  }
+}
+
+// The same from an fp8 K tile and fp8 Q registers.
+__device__ __forceinline__ void scores8(Scores &x, const u16 *bk, const FwdState &st,
+                                        const Nat8Off &no) {
+  x[0] = f32x16{};
+  x[1] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    x[0] = mfma32_f8(lds_nat8(bk, 0, kk, no), st.q8[kk], x[0]);
+    x[1] = mfma32_f8(lds_nat8(bk, 32, kk, no), st.q8[kk], x[1]);
   }
 }
 
@@ -131,6 +208,7 @@ __device__ __forceinline__ void pv_block(FwdState &st, const bf16x8 (&pb)[4], co
 
 constexpr int kWaves = 8;  // waves per workgroup, 32 query vectors each
 
+template <bool QK8>
 __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingArgs a) {
   // two K and two V tiles; separate objects so the LDS loads into one
   // buffer never order the reads of another
@@ -155,7 +233,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
   const int bound = valid ? (t.src ? a.bound_branch[row] : a.bound_main[row]) : -1;
 
   FwdState st;
-  {
+  if constexpr (QK8) {
+    // fp8 rows are 128 bytes: this lane's bytes 64 kk + 32 hf .. + 31
+    const char *qp = reinterpret_cast<const char *>(Q) + (int64_t(row) * a.hq + h) * 128 + hf * 32;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4 lo = valid ? *reinterpret_cast<const u32x4 *>(qp + 64 * kk) : u32x4{0, 0, 0, 0};
+      const u32x4 hi = valid ? *reinterpret_cast<const u32x4 *>(qp + 64 * kk + 16) : u32x4{0, 0, 0, 0};
+      st.q8[kk] = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+                        int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+    }
+  } else {
     const u16 *qp = Q + (int64_t(row) * a.hq + h) * 128 + hf * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -173,9 +261,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
   const int C = a.C, r = a.r, n_local = a.n_local, nseg = 2 * C;
 
   const NatOff no = nat_offsets(lane);
+  const Nat8Off no8 = nat8_offsets(lane);
   const TrOff to = tr_offsets(lane);
   const DmaOff<kWaves> dof =
       dma_offsets<kWaves>(wave, lane, [&](int rr) { return int64_t(rr) * rs; });
+  // fp8 K: rows of hkv * 128 bytes
+  const uint32_t dof8 = dma8_offset(wave, lane, rs);
+  const char *K8 = reinterpret_cast<const char *>(a.k);
   auto rec = [&](const Blk &b) {
     BlkRec q;
     if (b.sg >= nseg) {
@@ -194,7 +286,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
   // rows of the block past the chunk's visible end are not read (their
   // scores are masked)
   auto load = [&](u16 *dk, u16 *dv, const BlkRec &q) {
-    dma_tile64_buf<kWaves>(dk, buf_rsrc(K + q.off, q.bytes), dof, wave);
+    if constexpr (QK8) {
+      // same rows at one byte per element: the element offset is the byte
+      // offset, and the extent is half the bf16 one
+      dma_tile64_f8(dk, buf_rsrc(K8 + q.off, q.bytes / 2), dof8, wave);
+    } else {
+      dma_tile64_buf<kWaves>(dk, buf_rsrc(K + q.off, q.bytes), dof, wave);
+    }
     dma_tile64_buf<kWaves>(dv, buf_rsrc(V + q.off, q.bytes), dof, wave);
   };
 
@@ -222,7 +320,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
       }
       if (wave_active) {
         Scores x;
-        scores(x, KC, st, no);
+        if constexpr (QK8)
+          scores8(x, KC, st, no8);
+        else
+          scores(x, KC, st, no);
         if (cur.need) mask_block(x, min(cur.lim, bound - cur.pos0) - 4 * hf);
         if (first) {
           // every real row sees the first key of the first block
@@ -289,11 +390,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
   }
 }
 
+// Both instances are instantiated explicitly: with only the implicit
+// instantiation in launch_fwd_ring_fp8, hipcc's host pass referenced the
+// fp8 instance's launch stub without emitting it.
+template __global__ void fwd_ring_bf16_kernel<false>(FwdRingArgs);
+template __global__ void fwd_ring_bf16_kernel<true>(FwdRingArgs);
+
 }  // namespace
 
 hipError_t launch_fwd_ring_bf16(const FwdRingArgs &a, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_ring_bf16_kernel, dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
+  hipLaunchKernelGGL(fwd_ring_bf16_kernel<false>, dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_ring_fp8(const FwdRingArgs &a, int n_tiles, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_ring_bf16_kernel<true>, dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 

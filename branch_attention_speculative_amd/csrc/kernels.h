@@ -93,6 +93,7 @@ struct F32Shape {
 };
 
 hipError_t launch_fwd_ring_bf16(const FwdRingArgs &a, int n_tiles, hipStream_t s);
+hipError_t launch_fwd_ring_fp8(const FwdRingArgs &a, int n_tiles, hipStream_t s);
 hipError_t launch_fwd_branch(const FwdBranchArgs &a, int n_tiles, int dtype, int maxb, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdPreArgs &a, int dtype, hipStream_t s);
 hipError_t launch_bwd_branch(const BwdBranchArgs &a, int n_tiles, int dtype, int maxb, hipStream_t s);

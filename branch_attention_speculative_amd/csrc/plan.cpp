@@ -390,6 +390,8 @@ extern "C" ba_status ba_plan_create(const int32_t *seqlens, int32_t n_seqs, int3
       if (d != 128) return fail(BA_E_UNSUPPORTED, "bf16 path supports d == 128");
     } else if (dtype == BA_FP32) {
       if (d != 64 && d != 128) return fail(BA_E_UNSUPPORTED, "fp32 path supports d == 64 or 128");
+    } else if (dtype == BA_FP8) {
+      if (d != 128) return fail(BA_E_UNSUPPORTED, "fp8 path supports d == 128");
     } else {
       return fail(BA_E_INVALID, "unknown dtype");
     }

@@ -77,7 +77,13 @@ typedef enum {
   BA_E_OOM = 5          /* host or device allocation failed */
 } ba_status;
 
-typedef enum { BA_BF16 = 0, BA_FP32 = 1 } ba_dtype;
+/* Element types. BA_FP8: q, k, qb, kb hold OCP fp8 E4M3 codes (1 byte:
+ * exponent bias 7, no infinities, 0x7F/0xFF NaN); v, vb, o, ob are bf16; lse
+ * fp32. The scores are then formed by fp8 matrix-core products with fp32
+ * accumulation, everything after them as for BA_BF16. Per-tensor fp8 scale
+ * factors of Q and K fold into the softmax scale (s = scale * <q, k>).
+ * Forward only: branch_attn_bwd returns BA_E_UNSUPPORTED for such a plan. */
+typedef enum { BA_BF16 = 0, BA_FP32 = 1, BA_FP8 = 2 } ba_dtype;
 
 typedef enum {
   BA_BRANCH_NONE = 0,         /* main rows only: plain causal zigzag ring attention */
@@ -133,8 +139,8 @@ typedef struct {
  *                     of real tokens, strictly increasing (NULL/0 otherwise).
  *   branch_lens       block kinds: per-anchor block length (NULL = uniform).
  *   hq, hkv, d, dtype head configuration the plan's work lists are built for.
- * Supported: hq % hkv == 0 with hq/hkv a power of two <= 64; bf16 needs d == 128,
- * fp32 takes d == 64 or 128; branch lengths 1..64.
+ * Supported: hq % hkv == 0 with hq/hkv a power of two <= 64; bf16 and fp8 need
+ * d == 128, fp32 takes d == 64 or 128; branch lengths 1..64.
  * Returns BA_E_INVALID / BA_E_UNSUPPORTED with *out untouched on error.
  * Partition rule: rainbus analysis, background on context parallelism (head
  * and tail chunk per rank) and method steps, step two (N/C tokens per rank).

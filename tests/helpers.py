@@ -33,8 +33,14 @@ def make_plan(ba, w):
 
 
 def to_device(torch, w, arr):
-    if w.dtype == "bf16":
-        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    """Encoded host input -> device tensor of the library's element type:
+    uint8 fp8 E4M3 codes -> float8_e4m3fn, uint16 bf16 bits -> bfloat16,
+    float32 kept."""
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint8:
+        t = torch.from_numpy(arr).view(torch.float8_e4m3fn)
+    elif arr.dtype == np.uint16:
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
     else:
         t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
     return t.cuda()

@@ -1,0 +1,126 @@
+"""GPU parity of the fp8 forward (dtype "fp8": Q, K, Qb, Kb as OCP fp8 E4M3
+codes, V, Vb, O, Ob bf16) through the C ABI, against the oracle fed the same
+decoded fp8 values. The pages name fp8 as a precision to watch for the
+online-softmax merge (rainbus analysis, weaknesses and improvements, item 4);
+the tolerances are the bf16 ones: O max-abs <= 2e-2 and rel-L2 <= 1e-2, LSE
+max-abs <= 1e-3. The inputs are the bf16 workloads' seeded N(0, 1) draws,
+encoded to E4M3 for the score operands."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import pack
+
+from helpers import LazyF32, inputs, lse_err, make_plan, max_abs, oracle_grouped, oracle_structs, \
+    rel_l2, say, subset_grouped, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import branch_attention_speculative_amd as ba
+    ba.lib()
+    return torch, ba
+
+
+def _fp8(w):
+    return workloads.Workload(w.name + "-fp8", w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.hq,
+                              w.hkv, w.d, "fp8", False, w.seed, anchors=w.anchors,
+                              branch_lens=w.branch_lens)
+
+
+def _check(name, go, wo, gl, wl):
+    e_o, r_o, e_l = max_abs(go, wo), rel_l2(go, wo), lse_err(gl, wl)
+    say(f"  {name}: max|dO|={e_o:.3e} relL2={r_o:.3e} max|dLSE|={e_l:.3e}")
+    assert e_o <= 2e-2 and r_o <= 1e-2 and e_l <= 1e-3, (name, e_o, r_o, e_l)
+
+
+def _run(env, w):
+    torch, ba = env
+    say(f"[case] fp8 {w.name}: lens={w.seqlens[:6]} C={w.C} r={w.r} kind={w.kind} "
+        f"heads={w.hq}/{w.hkv}")
+    lay, br = oracle_structs(w)
+    plan = make_plan(ba, w)
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    raw, dec = inputs(w, N, NB, names=["q", "k", "v", "qb", "kb", "vb"])
+    assert raw["q"].dtype == np.uint8 and raw["v"].dtype == np.uint16
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    o, lse, ob, lseb = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+    torch.cuda.synchronize()
+    ref = oracle_grouped(lay, br, *(dec[k] for k in ("q", "k", "v", "qb", "kb", "vb")))
+    _check("o", to_host(o), ref["o"], to_host(lse), ref["lse"])
+    if NB:
+        _check("ob", to_host(ob), ref["ob"], to_host(lseb), ref["lseb"])
+    return plan, dev
+
+
+@pytest.mark.parametrize("name", ["ttt32k_r", "dflash_r", "long256k_r", "dspark_r"])
+def test_fp8_forward_reduced_workloads(env, name):
+    _run(env, _fp8(workloads.make(name)))
+
+
+def _edge(name, lens, C, r, kind, depth, hq, hkv, anchors=None, blens=None):
+    seed = sum(ord(ch) for ch in name)
+    return workloads.Workload(name, lens, C, r, kind, depth, hq, hkv, 128, "fp8", False, seed,
+                              anchors=anchors, branch_lens=blens)
+
+
+@pytest.mark.parametrize("w", [
+    # plain causal ring attention, C=1, one-token and odd-length sequences
+    _edge("fp8-none-c1", [1, 2, 3, 130], 1, 0, pack.KIND_NONE, 0, 4, 2),
+    # sequences shorter than 2C (pad rows), a long ragged chunk, G=16
+    _edge("fp8-short-c8", [5, 3, 17, 1], 8, 5, pack.KIND_TTT, 2, 8, 2),
+    _edge("fp8-ragged", [1999], 3, 1, pack.KIND_TTT, 2, 8, 2),
+    _edge("fp8-g16", [257, 100], 4, 2, pack.KIND_BLOCK_CAUSAL, 0, 16, 1,
+          anchors=[3, 100, 256, 300], blens=[8, 16, 8, 16]),
+    # blocks of 1 and of 64 keys, bidirectional
+    _edge("fp8-block-edges", [40, 200], 2, 1, pack.KIND_BLOCK_BIDIR, 0, 16, 4,
+          anchors=[0, 39, 40, 150, 239], blens=[1, 64, 5, 64, 1]),
+], ids=lambda w: w.name)
+def test_fp8_forward_edge_cases(env, w):
+    _run(env, w)
+
+
+def test_fp8_forward_full_size_long256k_sampled(env):
+    """The 262,144-token share in fp8: the first and last 16 rows of both local
+    chunks with all their TTT branch rows, against the oracle's dense form of
+    that row subset."""
+    torch, ba = env
+    w = _fp8(workloads.make("long256k"))
+    say("[case] fp8 full-size long256k")
+    lay, br = oracle_structs(w)
+    plan = make_plan(ba, w)
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    raw = workloads.draw(w, N, NB, names=["q", "k", "v", "qb", "kb", "vb"])
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    o, lse, ob, lseb = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+    torch.cuda.synchronize()
+    c = int(lay["c"][0])
+    rows = np.array(sorted(set(range(16)) | set(range(c - 16, c)) | set(range(c, c + 16)) |
+                           set(range(2 * c - 16, 2 * c))), np.int64)
+    anch = np.nonzero(np.isin(br["anchor_row"], rows))[0]
+    L = {k: LazyF32(w, v) for k, v in raw.items()}
+    ref = subset_grouped(lay, br, L["q"], L["k"], L["v"], L["qb"], L["kb"], L["vb"], rows, anch)
+    brows = ref["branch_rows"]
+    ri = torch.tensor(rows, device="cuda")
+    bi = torch.tensor(brows, device="cuda", dtype=torch.long)
+    _check("o", to_host(o[ri]), ref["o"], to_host(lse[ri]), ref["lse"])
+    _check("ob", to_host(ob[bi]), ref["ob"], to_host(lseb[bi]), ref["lseb"])
+
+
+def test_fp8_backward_is_rejected(env):
+    torch, ba = env
+    w = _fp8(workloads.make("dflash_r"))
+    plan = make_plan(ba, w)
+    args = ba.BwdArgs(scale=0.0)
+    L = ba.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.branch_attn_bwd(plan.handle, ctypes.byref(args), stream) == 2  # BA_E_UNSUPPORTED
+    assert b"forward only" in L.ba_last_error()

@@ -49,7 +49,7 @@ class Workload:
     hq: int
     hkv: int
     d: int
-    dtype: str                      # "bf16" or "fp32"
+    dtype: str                      # "bf16", "fp32" or "fp8" (fp8 E4M3 q/k/qb/kb, bf16 rest)
     bwd: bool
     seed: int
     anchors: Optional[List[int]] = None
@@ -167,7 +167,42 @@ def bf16_bits_to_f32(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def _e4m3_table():
+    """Values of the 127 non-negative finite OCP fp8 E4M3 codes 0x00..0x7E
+    (exponent bias 7, subnormals at exponent field 0, no infinities, 0x7F is
+    NaN), in code order, which is also increasing value order."""
+    codes = np.arange(127)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+_E4M3 = _e4m3_table()
+E4M3_MAX = float(_E4M3[-1])  # 448
+
+
+def f32_to_e4m3_bits(x):
+    """float32 -> OCP fp8 E4M3 codes (uint8), round to nearest, ties to the
+    even code; magnitudes beyond 448 saturate to 448. Inputs are finite."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x).astype(np.float64), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3, a, side="left"), 0, 126)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - _E4M3[lo], _E4M3[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def e4m3_bits_to_f32(b):
+    b = np.asarray(b, dtype=np.uint8)
+    mag = _E4M3[np.minimum(b & 0x7F, 126)].astype(np.float32)
+    return np.where(b & 0x80, -mag, mag).astype(np.float32)
+
+
 TENSOR_ORDER = ["q", "k", "v", "qb", "kb", "vb", "do", "dob"]
+# tensors that an fp8 workload holds in fp8 E4M3 (the score operands); the
+# others stay bf16
+FP8_TENSORS = ("q", "k", "qb", "kb")
 
 
 def tensor_shapes(n_local, n_branch, C, hq, hkv, d):
@@ -181,7 +216,9 @@ def tensor_shapes(n_local, n_branch, C, hq, hkv, d):
 def _fill(w, tensor_id, shape, lo, n, out, chunk):
     rng = np.random.default_rng([w.seed, 1000 + tensor_id, lo // chunk])
     x = rng.standard_normal(n, dtype=np.float32)
-    if w.dtype == "bf16":
+    if out.dtype == np.uint8:
+        out[lo:lo + n] = f32_to_e4m3_bits(x)
+    elif w.dtype in ("bf16", "fp8"):
         out[lo:lo + n] = f32_to_bf16_bits(x)
     else:
         out[lo:lo + n] = x
@@ -204,7 +241,10 @@ def draw(w, n_local, n_branch, names=TENSOR_ORDER, chunk=1 << 22, threads=None):
             continue
         shp = shapes[nm]
         n = int(np.prod(shp))
-        buf = np.empty(n, np.uint16 if w.dtype == "bf16" else np.float32)
+        if w.dtype == "fp8" and nm in FP8_TENSORS:
+            buf = np.empty(n, np.uint8)
+        else:
+            buf = np.empty(n, np.uint16 if w.dtype in ("bf16", "fp8") else np.float32)
         out[nm] = buf
         for lo in range(0, n, chunk):
             jobs.append((t, shp, lo, min(chunk, n - lo), buf))
@@ -215,5 +255,11 @@ def draw(w, n_local, n_branch, names=TENSOR_ORDER, chunk=1 << 22, threads=None):
 
 
 def as_f32(w, arr):
-    """Decode a drawn tensor to float32 values (bf16 bit patterns widened)."""
-    return bf16_bits_to_f32(arr) if w.dtype == "bf16" else np.asarray(arr, np.float32)
+    """Decode a drawn tensor to float32 values: fp8 E4M3 codes (uint8) and
+    bf16 bit patterns (uint16) are widened exactly, float32 is kept."""
+    arr = np.asarray(arr)
+    if arr.dtype == np.uint8:
+        return e4m3_bits_to_f32(arr)
+    if arr.dtype == np.uint16:
+        return bf16_bits_to_f32(arr)
+    return np.asarray(arr, np.float32)
