@@ -154,6 +154,64 @@ def cpu_baseline(w, plan_info, raw, n_anchor_sample, seed=11):
     }
 
 
+def bench_proj(args, ba, torch, w, plan):
+    """The draft-layer projection of every main and branch row of the
+    workload: q, k, v = x W^T with per-head RMS norm and RoPE, bf16, at
+    model width --hidden. One step = both calls."""
+    info = plan.info
+    N, NB, hid = info["n_local_rows"], info["n_branch_rows"], args.hidden
+    nout = (w.hq + 2 * w.hkv) * w.d
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    xm = torch.randn((N, hid), generator=gen, device="cuda").to(torch.bfloat16)
+    xb = torch.randn((NB, hid), generator=gen, device="cuda").to(torch.bfloat16)
+    W = (torch.randn((nout, hid), generator=gen, device="cuda") / hid ** 0.5).to(torch.bfloat16)
+    qn = torch.ones(w.d, dtype=torch.bfloat16, device="cuda")
+    kn = torch.ones(w.d, dtype=torch.bfloat16, device="cuda")
+    om = ba.qkv_project(plan, xm, W, qn, kn)
+    ob = ba.qkv_project(plan, xb, W, qn, kn, branch=True)
+
+    def step():
+        ba.qkv_project(plan, xm, W, qn, kn, out=om)
+        ba.qkv_project(plan, xb, W, qn, kn, branch=True, out=ob)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ba.profile_enable(True, max_launches=4 * args.steps + 8)
+    ba.profile_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kern = ba.profile_read()
+    ba.profile_enable(False)
+    flop = 2.0 * (N + NB) * hid * nout
+    n, tot = kern.get("qkv_project", (0, 0.0))
+    kms = tot / args.steps
+    byt = 2.0 * ((N + NB) * hid + nout * hid + (N + NB) * nout)
+    out = {"metric": "draft-layer Q/K/V projection + RMS norm + RoPE, TFLOP/s (1 GPU) and % of bf16 "
+                     "MFMA peak", "value": flop / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (random bf16 hidden states and weights)",
+           "config": {"workload": f"{describe(w, info)}; projection at hidden {hid}, "
+                                  f"{w.hq}/{w.hkv} heads of {w.d}", "rows": N + NB, "hidden": hid,
+                      "out_features": nout, "flop_per_step": flop},
+           "pct_of_peak": 100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "roofline": {"kernel": "qkv_project", "bound": "mfma",
+                        "achieved": flop / (kms * 1e-3) / 1e12 if kms else None,
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": flop / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS if kms else None,
+                        "traffic": None, "algorithmic_bytes": byt},
+           "cpu_baseline": None, "kernels": {"qkv_project": {"launches_per_step": n / args.steps,
+                                                             "ms_per_step": kms}}}
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +229,11 @@ def main():
                          "(0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--stage", default="attention", choices=["attention", "proj"],
+                    help="proj: time the draft-layer projection (ba_qkv_project) of the "
+                         "workload's main and branch rows instead, at --hidden")
+    ap.add_argument("--hidden", type=int, default=4096,
+                    help="model width of the projection stage (Qwen3-8B: 4096)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: Q/K/Qb/Kb as fp8 E4M3, V bf16, forward only (a step is the "
                          "forward; the metric and peak change accordingly)")
@@ -203,6 +266,8 @@ def main():
     info = plan.info
     N, NB = info["n_local_rows"], info["n_branch_rows"]
     print(f"[bench] {describe(w, info)}", file=sys.stderr, flush=True)
+    if args.stage == "proj":
+        return bench_proj(args, ba, torch, w, plan)
     raw = workloads.draw(w, N, NB, names=workloads.TENSOR_ORDER if w.bwd else
                          ["q", "k", "v", "qb", "kb", "vb"])
 

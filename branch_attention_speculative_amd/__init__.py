@@ -64,6 +64,12 @@ class BwdArgs(ctypes.Structure):
                [("workspace_bytes", ctypes.c_size_t)]
 
 
+class ProjArgs(ctypes.Structure):
+    _fields_ = [("target", ctypes.c_int32), ("step", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float)] + \
+               [(n, ctypes.c_void_p) for n in ("x", "w", "q_norm", "k_norm", "q", "k", "v")]
+
+
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
                 ("total_ms", ctypes.c_double)]
@@ -108,6 +114,8 @@ def lib():
         L.ba_plan_get_worklist.argtypes = [ctypes.c_void_p, ctypes.c_int32,
                                            ctypes.POINTER(_c_i32p), ctypes.POINTER(ctypes.c_int64),
                                            ctypes.POINTER(ctypes.c_int32)]
+        L.ba_qkv_project.restype = ctypes.c_int
+        L.ba_qkv_project.argtypes = [ctypes.c_void_p, ctypes.POINTER(ProjArgs), ctypes.c_void_p]
         L.ba_status_str.restype = ctypes.c_char_p
         L.ba_status_str.argtypes = [ctypes.c_int]
         L.ba_last_error.restype = ctypes.c_char_p
@@ -378,6 +386,50 @@ def bwd(plan, q, k, v, qb, kb, vb, o, lse, ob, lseb, do, dob, scale=0.0, workspa
         _check(lib().branch_attn_bwd(plan.handle, ctypes.byref(a), ctypes.c_void_p(stream)),
                "branch_attn_bwd")
     return dq, dk, dv, dqb, dkb, dvb
+
+
+def qkv_project(plan, x, w, q_norm=None, k_norm=None, branch=False, step=-1, rope_theta=1e6,
+                eps=1e-6, out=None):
+    """Draft-layer projection (``ba_qkv_project``): q, k, v of the rows of
+    hidden states ``x`` [rows, hidden] with ``w`` [(hq + 2 hkv) d, hidden],
+    per-head RMS norm of q and k when ``q_norm``/``k_norm`` [d] are given, and
+    RoPE at each row's position (``rope_theta <= 0``: none). Main rows
+    (branch=False) give q [N, hq, d], k, v [N, hkv, d]; branch rows give
+    qb [NB, hq, d], kb, vb [NB, hkv, d]; ``step = j`` takes one row per local
+    anchor (a TTT pass) and fills branch row j of every anchor in ``out``
+    (required then). Returns (q, k, v)."""
+    torch = _torch()
+    dev = x.device
+    i = plan.info
+    hq, hkv, d = i["hq"], i["hkv"], i["d"]
+    hidden = x.shape[1]
+    rows = i["n_branch_rows"] if branch else i["n_local_rows"]
+    if step >= 0:
+        if out is None:
+            raise ValueError("a TTT step pass fills given qb/kb/vb tensors: pass out=(qb, kb, vb)")
+        _expect("x", x, (i["n_local_anchors"], hidden), torch.bfloat16, dev)
+    else:
+        _expect("x", x, (rows, hidden), torch.bfloat16, dev)
+    _expect("w", w, ((hq + 2 * hkv) * d, hidden), torch.bfloat16, dev)
+    for name, t in (("q_norm", q_norm), ("k_norm", k_norm)):
+        if t is not None:
+            _expect(name, t, (d,), torch.bfloat16, dev)
+    if out is None:
+        out = (torch.empty((rows, hq, d), dtype=torch.bfloat16, device=dev),
+               torch.empty((rows, hkv, d), dtype=torch.bfloat16, device=dev),
+               torch.empty((rows, hkv, d), dtype=torch.bfloat16, device=dev))
+    q, k, v = out
+    _expect("q", q, (rows, hq, d), torch.bfloat16, dev)
+    _expect("k", k, (rows, hkv, d), torch.bfloat16, dev)
+    _expect("v", v, (rows, hkv, d), torch.bfloat16, dev)
+    a = ProjArgs(target=1 if branch else 0, step=int(step), hidden=int(hidden),
+                 rope_theta=float(rope_theta), norm_eps=float(eps), x=_ptr(x), w=_ptr(w),
+                 q_norm=_ptr(q_norm), k_norm=_ptr(k_norm), q=_ptr(q), k=_ptr(k), v=_ptr(v))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _check(lib().ba_qkv_project(plan.handle, ctypes.byref(a), ctypes.c_void_p(stream)),
+               "ba_qkv_project")
+    return q, k, v
 
 
 def profile_enable(on=True, max_launches=4096):

@@ -26,7 +26,7 @@ CFLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["plan.cpp", "api.hip", "fwd_ring.hip", "bwd_ring.hip", "branch.hip", "ring_f32.hip",
-           "probe.hip"]
+           "probe.hip", "proj.hip"]
 
 
 def _compile(src):

@@ -501,6 +501,74 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
   }
 }
 
+extern "C" ba_status ba_qkv_project(const ba_plan *p, const ba_proj_args *a, void *stream) {
+  try {
+    ba_status st = check_plan(p);
+    if (st != BA_OK) return st;
+    if (a == nullptr) return fail(BA_E_INVALID, "args is NULL");
+    if (p->dtype != BA_BF16 || p->d != 128)
+      return fail(BA_E_UNSUPPORTED, "the projection supports bf16 plans with d == 128");
+    if (a->target != 0 && a->target != 1) return fail(BA_E_INVALID, "target must be 0 or 1");
+    if (a->hidden < 64 || a->hidden % 64 != 0)
+      return fail(BA_E_INVALID, "hidden must be a positive multiple of 64");
+    if (int64_t(a->hidden) * 256 > (int64_t(1) << 31))
+      return fail(BA_E_UNSUPPORTED, "hidden too large for 32-bit tile offsets");
+    if (!std::isfinite(a->rope_theta) || !std::isfinite(a->norm_eps) || a->norm_eps < 0.f)
+      return fail(BA_E_INVALID, "rope_theta must be finite and norm_eps finite and >= 0");
+    if ((a->q_norm == nullptr) != (a->k_norm == nullptr))
+      return fail(BA_E_INVALID, "give both q_norm and k_norm or neither");
+    int64_t rows = 0;
+    if (a->target == 0) {
+      if (a->step != -1) return fail(BA_E_INVALID, "step applies to branch rows only");
+      rows = p->n_local;
+    } else if (a->step == -1) {
+      rows = p->n_branch;
+    } else {
+      if (p->kind != BA_BRANCH_TTT)
+        return fail(BA_E_INVALID, "a step pass needs a TTT plan (every anchor has every step)");
+      if (a->step < 0 || a->step >= p->depth_or_block)
+        return fail(BA_E_INVALID, "step must be -1 or in 0 .. depth - 1");
+      rows = int64_t(p->anchor_row.size());
+    }
+    if (rows == 0) return BA_OK;
+    if (!a->x || !a->w || !a->q || !a->k || !a->v)
+      return fail(BA_E_INVALID, "x, w, q, k and v are required");
+    for (const void *ptr : {a->x, a->w, (const void *)a->q, (const void *)a->k, (const void *)a->v,
+                            a->q_norm, a->k_norm})
+      if (!aligned16(ptr)) return fail(BA_E_INVALID, "every pointer must be 16-byte aligned");
+    if (rows * int64_t(a->hidden) * 2 > (int64_t(1) << 40))
+      return fail(BA_E_UNSUPPORTED, "x too large");
+    ba::ProjArgs k{};
+    k.x = a->x;
+    k.w = a->w;
+    k.q_norm = a->q_norm;
+    k.k_norm = a->k_norm;
+    k.q = a->q;
+    k.k = a->k;
+    k.v = a->v;
+    k.bound_main = p->dev.bound_main;
+    k.branch_off = p->dev.branch_off;
+    k.b_anchor = p->dev.b_anchor;
+    k.anchor_pos = p->dev.anchor_pos;
+    k.nrows = int32_t(rows);
+    k.hidden = a->hidden;
+    k.hq = p->hq;
+    k.hkv = p->hkv;
+    k.target = a->target;
+    k.step = a->step;
+    k.rope = a->rope_theta > 0.f ? 1 : 0;
+    k.eps = a->norm_eps;
+    for (int j = 0; j < 64; ++j)
+      k.inv_freq[j] = k.rope ? std::pow(double(a->rope_theta), -2.0 * j / 128.0) : 0.0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("qkv_project", s, [&] { return ba::launch_qkv_project(k, s); });
+    if (e != hipSuccess) return hip_fail("qkv_project launch", e);
+    return BA_OK;
+  } catch (...) {
+    return fail(BA_E_INVALID, "unexpected error in ba_qkv_project");
+  }
+}
+
 extern "C" ba_status ba_profile_enable(int32_t on, int32_t max_launches) {
   Profiler &P = prof();
   std::lock_guard<std::mutex> g(P.mu);

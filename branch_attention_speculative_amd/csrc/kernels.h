@@ -92,6 +92,23 @@ struct F32Shape {
   float scale, scale_log2;
 };
 
+// Draft-layer projection: q, k, v of rows of hidden states, per-head RMS norm
+// of q and k, RoPE at each row's position, written in the attention layouts.
+struct ProjArgs {
+  const void *x, *w, *q_norm, *k_norm;  // bf16; q_norm/k_norm NULL: no norm
+  void *q, *k, *v;
+  const int32_t *bound_main;             // main rows: position, -1 for pads
+  const int32_t *branch_off, *b_anchor, *anchor_pos;
+  int32_t nrows, hidden, hq, hkv;
+  int32_t target;  // 0: main rows, 1: branch rows
+  int32_t step;    // branch rows: -1 all rows; j >= 0 step j of every local anchor
+  int32_t rope;
+  float eps;
+  double inv_freq[64];  // theta^(-2j/128)
+};
+
+hipError_t launch_qkv_project(const ProjArgs &a, hipStream_t s);
+
 hipError_t launch_fwd_ring_bf16(const FwdRingArgs &a, int n_tiles, hipStream_t s);
 hipError_t launch_fwd_ring_fp8(const FwdRingArgs &a, int n_tiles, hipStream_t s);
 hipError_t launch_fwd_branch(const FwdBranchArgs &a, int n_tiles, int dtype, int maxb, hipStream_t s);

@@ -233,6 +233,45 @@ ba_status branch_attn_fwd_static(const ba_plan *plan, const ba_fwd_args *args, v
  */
 ba_status branch_attn_bwd(const ba_plan *plan, const ba_bwd_args *args, void *stream);
 
+/*
+ * Draft-layer projection: the step of the draft forward that produces the
+ * attention inputs (rainbus analysis, method steps, step four: EAGLE-3's
+ * training-time-test passes, DFlash's whole block; paperlens walkthrough,
+ * "The two walls"). For rows of draft hidden states x:
+ *   y = x W^T, split into hq q heads, hkv k heads, hkv v heads of d = 128;
+ *   q and k per head: y / sqrt(mean(y^2) + norm_eps) * norm weight (when
+ *     q_norm/k_norm are given);
+ *   q and k: rotary embedding at the row's position p, rotate-half form:
+ *     (y_j, y_{j+64}) turns by p * rope_theta^(-2j/128), j < 64 (when
+ *     rope_theta > 0).
+ * Positions: a main row sits at its position in its sequence; branch row j
+ * of the anchor at position p at p + 1 + j (the token it stands for). Pad
+ * main rows are written as zeros.
+ * Layouts (bf16, contiguous):
+ *   target 0, main rows: x [N, hidden] in local row order -> q [N, hq, d];
+ *     k, v [N, hkv, d] (this rank's own shard of the k/v arrays).
+ *   target 1, step -1, branch rows: x [NB, hidden] in branch-row order ->
+ *     qb [NB, hq, d], kb, vb [NB, hkv, d].
+ *   target 1, step j (TTT plans, 0 <= j < depth): x [A, hidden], one row per
+ *     local anchor in anchor order (the step-major input of one TTT pass) ->
+ *     branch row j of every anchor in qb, kb, vb; other rows are untouched.
+ *   w [(hq + 2 hkv) d, hidden]: q heads, then k heads, then v heads.
+ *   q_norm, k_norm [d], both or neither.
+ * Needs a bf16 plan with d == 128 (BA_E_UNSUPPORTED otherwise), hidden a
+ * positive multiple of 64. Enqueue only; allocates nothing.
+ */
+typedef struct {
+  int32_t target;     /* 0: main rows, 1: branch rows */
+  int32_t step;       /* -1, or a TTT step (target 1) */
+  int32_t hidden;
+  float rope_theta;   /* <= 0: no rotary embedding */
+  float norm_eps;
+  const void *x, *w, *q_norm, *k_norm;
+  void *q, *k, *v;
+} ba_proj_args;
+
+ba_status ba_qkv_project(const ba_plan *plan, const ba_proj_args *args, void *stream);
+
 const char *ba_status_str(ba_status s);
 const char *ba_last_error(void);
 
