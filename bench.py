@@ -234,6 +234,8 @@ def main():
                          "workload's main and branch rows instead, at --hidden")
     ap.add_argument("--hidden", type=int, default=4096,
                     help="model width of the projection stage (Qwen3-8B: 4096)")
+    ap.add_argument("--walk", default="auto", choices=["auto", "segments", "runs"],
+                    help="key walk of the forward and dQ kernels (auto: chosen by chunk size)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: Q/K/Qb/Kb as fp8 E4M3, V bf16, forward only (a step is the "
                          "forward; the metric and peak change accordingly)")
@@ -259,10 +261,11 @@ def main():
             sys.exit(2)
         w = dataclasses.replace(w, name=f"ttt{args.tokens}", seqlens=[args.tokens])
     fp8 = args.dtype == "fp8"
-    if fp8:
-        w = dataclasses.replace(w, dtype="fp8", bwd=False)
+    # a step is fwd+bwd for bf16 (every workload); the fp8 path is forward only
+    w = dataclasses.replace(w, dtype="fp8", bwd=False) if fp8 else dataclasses.replace(w, bwd=True)
     plan = ba.Plan(w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.anchors, w.branch_lens,
                    w.hq, w.hkv, w.d, w.dtype).upload()
+    plan.set_walk(args.walk)
     info = plan.info
     N, NB = info["n_local_rows"], info["n_branch_rows"]
     print(f"[bench] {describe(w, info)}", file=sys.stderr, flush=True)
@@ -372,7 +375,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": describe(w, info), "tokens": int(sum(w.seqlens)),
                    "cp_degree": w.C, "cp_rank": w.r, "local_rows": N, "branch_rows": NB,
-                   "pairs_per_head": pairs, "flop_per_step": flop_step},
+                   "pairs_per_head": pairs, "flop_per_step": flop_step,
+                   "key_walk": "run list" if info["run_walk"] else "segments"},
         "pct_of_peak": 100.0 * tflops / peak,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -36,7 +36,7 @@ _c_i32p = ctypes.POINTER(ctypes.c_int32)
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_seqs", "cp_degree", "cp_rank", "kind", "hq", "hkv", "d", "dtype",
-                 "max_branch_len", "reserved")] + \
+                 "max_branch_len", "run_walk")] + \
                [(n, ctypes.c_int64) for n in
                 ("n_local_rows", "n_pad_rows", "n_local_anchors", "n_branch_rows",
                  "pairs_main", "pairs_prefix", "pairs_local", "pairs_total")] + \
@@ -97,6 +97,8 @@ def lib():
                                      ctypes.POINTER(ctypes.c_void_p)]
         L.ba_plan_upload.restype = ctypes.c_int
         L.ba_plan_upload.argtypes = [ctypes.c_void_p]
+        L.ba_plan_set_walk.restype = ctypes.c_int
+        L.ba_plan_set_walk.argtypes = [ctypes.c_void_p, ctypes.c_int32]
         L.ba_plan_get_info.restype = ctypes.c_int
         L.ba_plan_get_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(PlanInfo)]
         L.ba_plan_get_indices.restype = ctypes.c_int
@@ -199,6 +201,13 @@ class Plan:
         if n.value == 0:
             return np.zeros((0, w.value), np.int32)
         return np.ctypeslib.as_array(ptr, shape=(n.value * w.value,)).reshape(n.value, w.value).copy()
+
+    def set_walk(self, mode):
+        """Key walk of the forward and dQ kernels: "auto", "segments" or "runs"."""
+        _check(lib().ba_plan_set_walk(self._h, {"auto": 0, "segments": 1, "runs": 2}[mode]),
+               "ba_plan_set_walk")
+        self.info = self._info()
+        return self
 
     def upload(self):
         """Copy index arrays and work lists to the current HIP device."""

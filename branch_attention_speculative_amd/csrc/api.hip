@@ -313,6 +313,7 @@ ba_status fwd_impl(const ba_plan *p, const ba_fwd_args *a, void *workspace, size
     ra.d = p->d;
     ra.scale = scale;
     ra.scale_log2 = scale * ba::kLog2eHost;
+    ra.runs = ba::uses_run_walk(*p) ? 1 : 0;
     hipError_t e;
     if (p->dtype == BA_BF16) {
       e = timed("fwd_ring", s, [&] { return ba::launch_fwd_ring_bf16(ra, int(p->qtiles.size()), s); });
@@ -456,6 +457,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     q.d = p->d;
     q.scale = scale;
     q.scale_log2 = scale * ba::kLog2eHost;
+    q.runs = ba::uses_run_walk(*p) ? 1 : 0;
 
     ba::BwdDkdvArgs k{};
     k.q = a->q;

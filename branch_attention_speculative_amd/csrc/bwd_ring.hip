@@ -71,11 +71,15 @@ __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[
 
 constexpr int kDqWaves = 8;  // waves per dQ workgroup (32 query vectors each)
 
+// RUNS: walk the tile's run list (else the segments)
+template <bool RUNS>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sK0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sV0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sK1[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sV1[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) RunSeg sRuns[RUNS ? kMaxRuns : 1];
+  __shared__ int sNRuns;
 
   const QTile t = a.qtiles[blockIdx.x];
   if (t.nrows == 0) return;
@@ -134,12 +138,26 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
   lds_zero(sV0, kBN * kRS, tid, kDqWaves * 64);
   lds_zero(sK1, kBN * kRS, tid, kDqWaves * 64);
   lds_zero(sV1, kBN * kRS, tid, kDqWaves * 64);
+  if constexpr (RUNS) {
+    if (wave == 0) build_runs(sRuns, &sNRuns, t, a.C, a.r, a.n_local, lane);
+  }
   __syncthreads();
 
   int sg, j0;
   Seg s;
-  first_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
-  const int nseg = 2 * a.C;
+  int nseg = 2 * a.C;  // end of the walk: segments, or runs
+  if constexpr (RUNS) {
+    nseg = uniform_int(sNRuns);
+    first_run(sg, j0, s, sRuns, nseg);
+  } else {
+    first_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+  }
+  auto advance = [&]() {
+    if constexpr (RUNS)
+      next_run<kBN>(sg, j0, s, sRuns, nseg);
+    else
+      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+  };
   if (sg < nseg) dma_kv(s, j0, sK0, sV0);
   dma_wait();
   __syncthreads();
@@ -147,7 +165,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
     {
       const Seg cs = s;
       const int cj0 = j0;
-      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+      advance();
       if (sg < nseg) dma_kv(s, j0, sK1, sV1);
       if (wave_active) {
         const bool need = cj0 + kBN > cs.n_full;
@@ -161,7 +179,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
     {
       const Seg cs = s;
       const int cj0 = j0;
-      next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
+      advance();
       if (sg < nseg) dma_kv(s, j0, sK0, sV0);
       if (wave_active) {
         const bool need = cj0 + kBN > cs.n_full;
@@ -491,11 +509,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     }
 }
 
+template __global__ void bwd_dq_bf16_kernel<false>(BwdDqArgs);
+template __global__ void bwd_dq_bf16_kernel<true>(BwdDqArgs);
+
 }  // namespace
 
 hipError_t launch_bwd_dq_bf16(const BwdDqArgs &a, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dq_bf16_kernel, dim3(n_tiles), dim3(kDqWaves * 64), 0, s, a);
+  if (a.runs)
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<true>), dim3(n_tiles), dim3(kDqWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<false>), dim3(n_tiles), dim3(kDqWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -134,15 +134,28 @@ struct BlkRec {
 // is x[v / 16][v % 16].
 typedef f32x16 Scores[2];
 
-// S^T = K Q^T for one 64-key block.
+// S^T = K Q^T for one 64-key block. The K operands of step ks + 1 are read
+// from LDS before the products of step ks, and the scheduling barrier keeps
+// the compiler from sinking them back next to their use (measured about 1%
+// faster on the long workload than reading each operand just before its
+// product).
 __device__ __forceinline__ void scores(Scores &x, const u16 *bk, const FwdState &st,
                                        const NatOff &no) {
   x[0] = f32x16{};
   x[1] = f32x16{};
+  bf16x8 a0 = lds_nat_o(bk, 0, 0, no), a1 = lds_nat_o(bk, 32, 0, no);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    x[0] = mfma32(lds_nat_o(bk, 0, ks, no), st.qreg[ks], x[0]);
-    x[1] = mfma32(lds_nat_o(bk, 32, ks, no), st.qreg[ks], x[1]);
+    bf16x8 n0 = a0, n1 = a1;
+    if (ks + 1 < 8) {
+      n0 = lds_nat_o(bk, 0, ks + 1, no);
+      n1 = lds_nat_o(bk, 32, ks + 1, no);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    x[0] = mfma32(a0, st.qreg[ks], x[0]);
+    x[1] = mfma32(a1, st.qreg[ks], x[1]);
+    a0 = n0;
+    a1 = n1;
   }
 }
 
@@ -208,7 +221,8 @@ __device__ __forceinline__ void pv_block(FwdState &st, const bf16x8 (&pb)[4], co
 
 constexpr int kWaves = 8;  // waves per workgroup, 32 query vectors each
 
-template <bool QK8>
+// QK8: fp8 Q/K (else bf16); RUNS: walk the tile's run list (else the segments)
+template <bool QK8, bool RUNS>
 __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingArgs a) {
   // two K and two V tiles; separate objects so the LDS loads into one
   // buffer never order the reads of another
@@ -216,6 +230,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
   __shared__ __attribute__((aligned(16))) u16 sK1[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sV0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sV1[kBN * kRS];
+  __shared__ __attribute__((aligned(16))) RunSeg sRuns[RUNS ? kMaxRuns : 1];
+  __shared__ int sNRuns;
 
   const QTile t = a.qtiles[blockIdx.x];
   if (t.nrows == 0) return;
@@ -258,7 +274,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
   const float c = a.scale_log2;
   const int64_t rs = int64_t(a.hkv) * 128;
   const int g = t.g;
-  const int C = a.C, r = a.r, n_local = a.n_local, nseg = 2 * C;
+  const int C = a.C, r = a.r, n_local = a.n_local;
+  int nseg = 2 * C;  // end of the walk: segments, or runs
 
   const NatOff no = nat_offsets(lane);
   const Nat8Off no8 = nat8_offsets(lane);
@@ -302,10 +319,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
   lds_zero(sV1, kBN * kRS, tid, kWaves * 64);
 
   Blk wk;  // the walker: one block ahead of the one computed
-  first_block<kBN>(wk.sg, wk.j0, wk.s, t, C, r, n_local);
+  auto advance = [&]() {
+    if constexpr (RUNS)
+      next_run<kBN>(wk.sg, wk.j0, wk.s, sRuns, nseg);
+    else
+      next_block<kBN>(wk.sg, wk.j0, wk.s, t, C, r, n_local);
+  };
+  if constexpr (RUNS) {
+    if (wave == 0) build_runs(sRuns, &sNRuns, t, C, r, n_local, lane);
+    __syncthreads();
+    nseg = uniform_int(sNRuns);
+    first_run(wk.sg, wk.j0, wk.s, sRuns, nseg);
+  } else {
+    first_block<kBN>(wk.sg, wk.j0, wk.s, t, C, r, n_local);
+  }
   BlkRec cur = rec(wk);
   if (cur.bytes) {  // else every row of the tile is a pad: O = 0, LSE = -inf
-    next_block<kBN>(wk.sg, wk.j0, wk.s, t, C, r, n_local);
+    advance();
     __syncthreads();  // LDS zeroed before any tile load lands
     load(sK0, sV0, cur);
     vm_wait<0>();
@@ -316,7 +346,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
       const BlkRec nxt = rec(wk);
       if (nxt.bytes) {
         load(KN, VN, nxt);
-        next_block<kBN>(wk.sg, wk.j0, wk.s, t, C, r, n_local);
+        advance();
       }
       if (wave_active) {
         Scores x;
@@ -390,23 +420,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_ring_bf16_kernel(FwdRingAr
   }
 }
 
-// Both instances are instantiated explicitly: with only the implicit
-// instantiation in launch_fwd_ring_fp8, hipcc's host pass referenced the
-// fp8 instance's launch stub without emitting it.
-template __global__ void fwd_ring_bf16_kernel<false>(FwdRingArgs);
-template __global__ void fwd_ring_bf16_kernel<true>(FwdRingArgs);
+// Every instance is instantiated explicitly: with only the implicit
+// instantiation in the launchers, hipcc's host pass referenced the fp8
+// instance's launch stub without emitting it.
+template __global__ void fwd_ring_bf16_kernel<false, false>(FwdRingArgs);
+template __global__ void fwd_ring_bf16_kernel<false, true>(FwdRingArgs);
+template __global__ void fwd_ring_bf16_kernel<true, false>(FwdRingArgs);
+template __global__ void fwd_ring_bf16_kernel<true, true>(FwdRingArgs);
 
 }  // namespace
 
 hipError_t launch_fwd_ring_bf16(const FwdRingArgs &a, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_ring_bf16_kernel<false>, dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
+  if (a.runs)
+    hipLaunchKernelGGL((fwd_ring_bf16_kernel<false, true>), dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_ring_bf16_kernel<false, false>), dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_ring_fp8(const FwdRingArgs &a, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_ring_bf16_kernel<true>, dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
+  if (a.runs)
+    hipLaunchKernelGGL((fwd_ring_bf16_kernel<true, true>), dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_ring_bf16_kernel<true, false>), dim3(n_tiles), dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct FwdRingArgs {
   int32_t n_local, n_branch, hq, hkv, G, log2G, C, r, d;
   float scale_log2;  // softmax scale * log2(e)
   float scale;
+  int32_t runs;      // walk each tile's run list (short chunks) instead of its segments
 };
 
 // Branch-local forward and the Eq. 2 merge with the main partial.
@@ -71,6 +72,7 @@ struct BwdDqArgs {
   const int32_t *bound_main, *bound_branch;
   int32_t n_local, n_branch, hq, hkv, G, log2G, C, r, d;
   float scale, scale_log2;
+  int32_t runs;  // as in FwdRingArgs
 };
 
 // Ring replay for dK/dV (key-stationary).

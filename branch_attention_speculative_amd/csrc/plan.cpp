@@ -364,6 +364,9 @@ static ba_status build(ba_plan &p, const int32_t *seqlens, const int32_t *anchor
   }
   p.ws_fwd = ws_fwd_bytes(p);
   p.ws_bwd = ws_bwd_bytes(p);
+  p.run_walk_auto = 1;
+  for (int32_t c : p.c)
+    if (c > kRunWalkMaxChunk) p.run_walk_auto = 0;
   return BA_OK;
 }
 
@@ -419,6 +422,13 @@ extern "C" ba_status ba_plan_create(const int32_t *seqlens, int32_t n_seqs, int3
   }
 }
 
+extern "C" ba_status ba_plan_set_walk(ba_plan *p, int32_t mode) {
+  if (p == nullptr) return fail(BA_E_INVALID, "plan is NULL");
+  if (mode < 0 || mode > 2) return fail(BA_E_INVALID, "walk mode must be 0, 1 or 2");
+  p->walk_mode = mode;
+  return BA_OK;
+}
+
 extern "C" ba_status ba_plan_get_info(const ba_plan *p, ba_plan_info *out) {
   if (p == nullptr || out == nullptr) return fail(BA_E_INVALID, "NULL argument");
   ba_plan_info i{};
@@ -431,6 +441,7 @@ extern "C" ba_status ba_plan_get_info(const ba_plan *p, ba_plan_info *out) {
   i.d = p->d;
   i.dtype = p->dtype;
   i.max_branch_len = p->max_branch_len;
+  i.run_walk = ba::uses_run_walk(*p) ? 1 : 0;
   i.n_local_rows = p->n_local;
   i.n_pad_rows = p->n_pad;
   i.n_local_anchors = int64_t(p->anchor_row.size());

@@ -16,6 +16,11 @@ constexpr int kKTileKeys = 128;   // keys per dK/dV tile
 constexpr int kKBlockVecs = 64;   // query vectors per dK/dV inner block
 constexpr int kMaxBranch = 64;    // longest branch the branch-local kernels accept
 constexpr int kNumXcd = 8;        // MI355X: 8 accelerator complex dies, WGs dispatched round-robin
+// The forward and dQ kernels walk a tile's keys through a run list built in
+// LDS when every sequence's chunk is at most this many rows, and through the
+// (step, chunk) segments otherwise (measured: the run list is faster on
+// chunks of hundreds of rows, slightly slower on chunks of 16K rows).
+constexpr int kRunWalkMaxChunk = 8192;
 
 // Query tile of the forward / dQ kernels: consecutive rows of one source
 // (main rows or branch rows) of one sequence chunk, times the G q-heads of one
@@ -89,6 +94,8 @@ struct ba_plan {
   int64_t n_local = 0, n_branch = 0, n_pad = 0;
   int64_t pairs_main = 0, pairs_prefix = 0, pairs_local = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
+  int32_t run_walk_auto = 0;  // every chunk <= kRunWalkMaxChunk
+  int32_t walk_mode = 0;      // 0: automatic, 1: segments, 2: run list (ba_plan_set_walk)
   ba::DevPlan dev;
   // guards dev: ba_plan_upload may run on several threads at once, and
   // fwd/bwd read dev under it
@@ -96,6 +103,10 @@ struct ba_plan {
 };
 
 namespace ba {
+// Whether the forward and dQ kernels walk run lists for this plan.
+inline bool uses_run_walk(const ba_plan &p) {
+  return p.walk_mode == 2 || (p.walk_mode == 0 && p.run_walk_auto != 0);
+}
 // Thread-local error detail used by every entry point.
 void set_error(const std::string &msg);
 const char *get_error();

@@ -178,6 +178,88 @@ __device__ __forceinline__ void next_block(int &sg, int &j0, Seg &s, const QTile
   }
 }
 
+// ---- run list (the walk for short chunks) ----------------------------------
+// The same walk as a list of runs built once per tile: the visible segments in
+// walk order, where a shard's head and tail chunk of the sequence become one
+// run of 2c keys when every row of the tile sees both in full (they are
+// adjacent rows of the shard, and then no key of the run needs masking). The
+// list lives in LDS and is walked by index, so the per-block walk logic is a
+// few scalar loads instead of the segment arithmetic: on workloads with short
+// chunks (hundreds of rows) that logic and the partial blocks at chunk ends
+// weigh more than on long chunks.
+constexpr int kMaxRuns = 128;  // 2 C segments, C <= 64
+
+struct RunSeg {
+  int n_hi, n_full, cpos0, pad;
+  int64_t krow;
+};
+
+__device__ __forceinline__ Seg run_seg(int sg, const QTile &t, int C, int r, int n_local) {
+  const int i = sg >> 1, half = sg & 1;
+  int sh = r - i;
+  if (sh < 0) sh += C;
+  const int tail = 2 * C - 1 - sh;
+  Seg s;
+  s.krow = int64_t(sh) * n_local + t.seq_off + int64_t(half) * t.c;
+  if (t.p_min >= (tail + 1) * t.c - 1) {
+    // every row sees both chunks in full (no pad row in the tile, no pad key
+    // in them): one run from the head chunk's first row; cpos0 is placed so
+    // that bound - cpos0 >= 2c - 1 for every row, i.e. nothing is masked
+    s.cpos0 = (tail - 1) * t.c;
+    s.n_hi = s.n_full = half ? 0 : 2 * t.c;
+    return s;
+  }
+  s.cpos0 = (half ? tail : sh) * t.c;
+  s.n_hi = min(max(t.p_max - s.cpos0 + 1, 0), t.c);
+  s.n_full = min(max(t.p_min - s.cpos0 + 1, 0), t.c);
+  return s;
+}
+
+// Built by one wave: segment sg = 64 j + lane, the live ones (n_hi > 0)
+// compacted in order with a ballot.
+__device__ __forceinline__ void build_runs(RunSeg *runs, int *n_runs, const QTile &t, int C, int r,
+                                           int n_local, int lane) {
+  int base = 0;
+  for (int sg0 = 0; sg0 < 2 * C; sg0 += 64) {
+    const int sg = sg0 + lane;
+    Seg s{0, 0, 0, 0};
+    if (sg < 2 * C) s = run_seg(sg, t, C, r, n_local);
+    const bool live = s.n_hi > 0;
+    const uint64_t m = __ballot(live);
+    const int at = base + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+    if (live) runs[at] = RunSeg{s.n_hi, s.n_full, s.cpos0, 0, s.krow};
+    base += __popcll(m);
+  }
+  if (lane == 0) *n_runs = base;
+}
+
+__device__ __forceinline__ Seg load_run(const RunSeg *runs, int k) {
+  const RunSeg v = runs[k];
+  Seg s;
+  s.n_hi = uniform_int(v.n_hi);
+  s.n_full = uniform_int(v.n_full);
+  s.cpos0 = uniform_int(v.cpos0);
+  const uint64_t kr = uint64_t(v.krow);
+  s.krow = int64_t((uint64_t(uint32_t(uniform_int(int(kr >> 32)))) << 32) |
+                   uint32_t(uniform_int(int(kr & 0xffffffffu))));
+  return s;
+}
+
+__device__ __forceinline__ void first_run(int &k, int &j0, Seg &s, const RunSeg *runs, int n_runs) {
+  k = 0;
+  j0 = 0;
+  if (n_runs > 0) s = load_run(runs, 0);
+}
+
+template <int BN>
+__device__ __forceinline__ void next_run(int &k, int &j0, Seg &s, const RunSeg *runs, int n_runs) {
+  j0 += BN;
+  if (j0 < s.n_hi) return;
+  j0 = 0;
+  if (++k < n_runs) s = load_run(runs, k);
+}
+
 // ---- precomputed per-lane offsets ----------------------------------------
 // swz(r) only depends on r & 15, so shifting a tile row by a multiple of 16
 // moves every address by a constant. The byte offsets below are computed

@@ -101,7 +101,9 @@ typedef struct ba_plan ba_plan; /* opaque, library-owned */
 typedef struct {
   int32_t n_seqs, cp_degree, cp_rank, kind, hq, hkv, d, dtype;
   int32_t max_branch_len;
-  int32_t reserved;
+  int32_t run_walk;        /* 1: the forward and dQ kernels walk per-tile run lists
+                              (chosen when every chunk is <= 8192 rows, or forced by
+                              ba_plan_set_walk); 0: they walk the (step, chunk) segments */
   int64_t n_local_rows;    /* N: rank-local main rows, pads included */
   int64_t n_pad_rows;      /* pad rows among them */
   int64_t n_local_anchors; /* anchors owned by this rank */
@@ -157,6 +159,14 @@ ba_status ba_plan_create(const int32_t *seqlens, int32_t n_seqs, int32_t cp_degr
 ba_status ba_plan_upload(ba_plan *plan);
 
 ba_status ba_plan_get_info(const ba_plan *plan, ba_plan_info *out);
+
+/* How the forward and dQ kernels walk each query tile's keys: mode 0 chooses
+ * by chunk size (a run list built per tile when every chunk is <= 8192 rows,
+ * the (step, chunk) segments otherwise), 1 forces the segments, 2 the run
+ * list. Both walks visit the same keys; results agree to summation order.
+ * For tests and measurement; takes effect at the next fwd/bwd call. Not
+ * thread-safe against concurrent fwd/bwd calls on the same plan. */
+ba_status ba_plan_set_walk(ba_plan *plan, int32_t mode);
 ba_status ba_plan_get_indices(const ba_plan *plan, ba_indices *out);
 void ba_plan_destroy(ba_plan *plan); /* frees host and device memory; NULL is a no-op */
 

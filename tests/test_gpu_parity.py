@@ -35,12 +35,14 @@ def env():
     return torch, ba
 
 
-def _run(env, w, with_bwd, oracle_dtype=np.float32, prep=None, threads=4):
+def _run(env, w, with_bwd, oracle_dtype=np.float32, prep=None, threads=4, walk=None):
     torch, ba = env
     say(f"[case] {w.name}: lens={w.seqlens[:6]}{'...' if len(w.seqlens) > 6 else ''} C={w.C} r={w.r} "
         f"kind={w.kind} depth/block={w.depth_or_block} heads={w.hq}/{w.hkv} d={w.d} {w.dtype}")
     lay, br = oracle_structs(w)
     plan = make_plan(ba, w)
+    if walk is not None:
+        plan.set_walk(walk)
     N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
     assert (N, NB) == (lay["n_local"], br["n_branch"])
     raw, dec = inputs(w, N, NB)
@@ -183,6 +185,23 @@ EDGES = [
 @pytest.mark.parametrize("w", EDGES, ids=[e.name for e in EDGES])
 def test_edge_cases(env, w):
     got, ref, _ = _run(env, w, with_bwd=True)
+    _check_fwd(w, got, ref)
+    _check_bwd(w, got, ref)
+
+
+@pytest.mark.parametrize("walk", ["segments", "runs"])
+@pytest.mark.parametrize("name", ["ttt32k_r", "dspark_r", "long256k_r", "short-c8", "c64",
+                                  "many-seqs", "ragged"])
+def test_both_key_walks(env, name, walk):
+    """The forward and dQ kernels walk a tile's keys either through the (step,
+    chunk) segments or through a run list built per tile (the planner picks
+    by chunk size); both are checked against the oracle, forward and
+    backward, on the same inputs."""
+    w = workloads.make(name) if name.endswith("_r") else next(e for e in EDGES if e.name == name)
+    w = workloads.Workload(w.name, w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.hq, w.hkv, w.d,
+                           w.dtype, True, w.seed, anchors=w.anchors, branch_lens=w.branch_lens)
+    got, ref, plan = _run(env, w, with_bwd=True, walk=walk)
+    assert plan.info["run_walk"] == (1 if walk == "runs" else 0)
     _check_fwd(w, got, ref)
     _check_bwd(w, got, ref)
 

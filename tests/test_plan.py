@@ -241,3 +241,24 @@ def test_binding_checks_the_caller_workspace():
         ba._workspace(torch.empty(8, 8, dtype=torch.uint8).t(), 1, cpu)
     with pytest.raises(ValueError, match="expected device"):
         ba._workspace(torch.empty(8, dtype=torch.uint8), 1, torch.device("cuda", 0))
+
+
+def test_key_walk_choice_by_chunk_size():
+    # run lists when every chunk is <= 8192 rows, segments otherwise; the
+    # override forces either and returns to the automatic choice with mode 0
+    ba = pytest.importorskip("branch_attention_speculative_amd")
+    short = ba.Plan([5000, 3000], 4, 0, 1, 2, hq=8, hkv=2, d=128, dtype="bf16")
+    assert short.info["run_walk"] == 1
+    long_ = ba.Plan([262144], 8, 0, 1, 2, hq=8, hkv=2, d=128, dtype="bf16")
+    assert long_.info["run_walk"] == 0  # chunks of 16384 rows
+    edge = ba.Plan([8192 * 16], 8, 0, 0, 0, hq=8, hkv=2, d=128, dtype="bf16")
+    assert edge.info["run_walk"] == 1  # exactly 8192-row chunks
+    long_.set_walk("runs")
+    assert long_.info["run_walk"] == 1
+    short.set_walk("segments")
+    assert short.info["run_walk"] == 0
+    short.set_walk("auto")
+    assert short.info["run_walk"] == 1
+    with pytest.raises(ba.BranchAttnError):
+        ba.lib()
+        _ = ba._check(ba.lib().ba_plan_set_walk(short.handle, 3), "ba_plan_set_walk")
