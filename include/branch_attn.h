@@ -240,6 +240,14 @@ ba_status branch_attn_fwd_static(const ba_plan *plan, const ba_fwd_args *args, v
  * Backward, recomputed from the merged LSE: Delta = rowsum(dO * O), then the
  * ring replay (dQ for every local row; dK/dV for every shard), the branch-local
  * backward, and the final sums. Enqueue only.
+ * Precision (bf16): as in bf16 matrix-core attention, O (in Delta), P (in the
+ * forward's P V) and dS are rounded to bf16. Each rounding leaves the row sum
+ * of dS slightly off its exact value 0, and dQ = scale * sum_k dS_k k_k picks
+ * up that residue times whatever component the keys of a row share. For
+ * keys whose shared component is up to a few times their spread the results
+ * stay within bf16 attention's usual error; far beyond that (scores of a row
+ * all shifted by hundreds of units together) dQ degrades in proportion to
+ * the shared component. dK and dV are not affected.
  */
 ba_status branch_attn_bwd(const ba_plan *plan, const ba_bwd_args *args, void *stream);
 
