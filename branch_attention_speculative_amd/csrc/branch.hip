@@ -56,32 +56,6 @@ __device__ __forceinline__ void ld8<float>(const float *p, int64_t i, float (&o)
   }
 }
 
-// load 8 consecutive elements as floats and keep a raw copy of them in LDS
-template <typename T>
-__device__ __forceinline__ void ld8_keep(const T *p, int64_t i, T *lds, float (&o)[8]);
-template <>
-__device__ __forceinline__ void ld8_keep<u16>(const u16 *p, int64_t i, u16 *lds, float (&o)[8]) {
-  const u32x4 x = *reinterpret_cast<const u32x4 *>(p + i);
-  *reinterpret_cast<u32x4 *>(lds) = x;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[2 * k] = __uint_as_float(x[k] << 16);
-    o[2 * k + 1] = __uint_as_float(x[k] & 0xffff0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void ld8_keep<float>(const float *p, int64_t i, float *lds, float (&o)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p + i);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + i + 4);
-  *reinterpret_cast<f32x4 *>(lds) = a;
-  *reinterpret_cast<f32x4 *>(lds + 4) = b;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    o[k] = a[k];
-    o[4 + k] = b[k];
-  }
-}
-
 // fp8 E4M3 codes (Q and K of the fp8 path): 8 consecutive bytes, 8-byte aligned
 template <>
 __device__ __forceinline__ void ld8<uint8_t>(const uint8_t *p, int64_t i, float (&o)[8]) {
@@ -113,6 +87,71 @@ __device__ __forceinline__ void ld4<float>(const float *p, int64_t i, float (&o)
   const f32x4 a = *reinterpret_cast<const f32x4 *>(p + i);
 #pragma unroll
   for (int k = 0; k < 4; ++k) o[k] = a[k];
+}
+
+// 8 consecutive elements as loaded (raw), and their conversion to floats: the
+// kernels issue every global load of a query vector before the arithmetic
+// that uses the first one, so that the loads' latencies overlap
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<u16> {
+  u32x4 x;
+};
+template <>
+struct Raw8<float> {
+  f32x4 a, b;
+};
+template <>
+struct Raw8<uint8_t> {
+  u32x2 x;
+};
+template <typename T>
+__device__ __forceinline__ Raw8<T> ldraw8(const T *p, int64_t i);
+template <>
+__device__ __forceinline__ Raw8<u16> ldraw8<u16>(const u16 *p, int64_t i) {
+  return {*reinterpret_cast<const u32x4 *>(p + i)};
+}
+template <>
+__device__ __forceinline__ Raw8<float> ldraw8<float>(const float *p, int64_t i) {
+  return {*reinterpret_cast<const f32x4 *>(p + i), *reinterpret_cast<const f32x4 *>(p + i + 4)};
+}
+template <>
+__device__ __forceinline__ Raw8<uint8_t> ldraw8<uint8_t>(const uint8_t *p, int64_t i) {
+  return {*reinterpret_cast<const u32x2 *>(p + i)};
+}
+__device__ __forceinline__ void cvt8(const Raw8<u16> &r, float (&o)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = __uint_as_float(r.x[k] << 16);
+    o[2 * k + 1] = __uint_as_float(r.x[k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void cvt8(const Raw8<float> &r, float (&o)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = r.a[k];
+    o[4 + k] = r.b[k];
+  }
+}
+__device__ __forceinline__ void cvt8(const Raw8<uint8_t> &r, float (&o)[8]) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(r.x[k]), false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(r.x[k]), true);
+    o[4 * k] = lo[0];
+    o[4 * k + 1] = lo[1];
+    o[4 * k + 2] = hi[0];
+    o[4 * k + 3] = hi[1];
+  }
+}
+// a raw copy into LDS (8 elements at lds, 16-byte aligned)
+__device__ __forceinline__ void keep8(const Raw8<u16> &r, u16 *lds) {
+  *reinterpret_cast<u32x4 *>(lds) = r.x;
+}
+__device__ __forceinline__ void keep8(const Raw8<float> &r, float *lds) {
+  *reinterpret_cast<f32x4 *>(lds) = r.a;
+  *reinterpret_cast<f32x4 *>(lds + 4) = r.b;
 }
 
 template <typename T>
@@ -178,6 +217,13 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
     const int nvis = a.bidir ? n : j + 1;
     const int kl0 = lo - base;
     const int64_t qh = int64_t(row) * a.hq + h;
+    Raw8<TQ> qr[QD / 8];
+    Raw8<float> mr[QD / 8];
+#pragma unroll
+    for (int dc = 0; dc < QD / 8; ++dc) qr[dc] = ldraw8<TQ>(QB, qh * DIM + sub * QD + dc * 8);
+#pragma unroll
+    for (int dc = 0; dc < QD / 8; ++dc) mr[dc] = ldraw8<float>(a.om, qh * DIM + sub * QD + dc * 8);
+    const float lm2 = a.lm[qh] * kLog2e;  // main-sequence LSE (log2)
     float s[MAXB];
 #pragma unroll
     for (int jj = 0; jj < MAXB; ++jj) s[jj] = 0.f;
@@ -185,7 +231,7 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
     for (int dc = 0; dc < QD / 8; ++dc) {
       const int d0 = sub * QD + dc * 8;
       float q8[8];
-      ld8<TQ>(QB, qh * DIM + d0, q8);
+      cvt8(qr[dc], q8);
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) {
         if (jj < nvis) {
@@ -219,7 +265,6 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
       lsum += s[jj];
     }
     const float lb2 = mb + log2f(lsum);  // branch-local LSE (log2)
-    const float lm2 = a.lm[qh] * kLog2e;   // main-sequence LSE (log2)
     // Eq. 2: l = log(e^lm + e^lb); weights e^(lm - l), e^(lb - l)
     const float hi = fmaxf(lm2, lb2);
     const float l2 = hi + log2f(fast_exp2(lm2 - hi) + fast_exp2(lb2 - hi));
@@ -244,7 +289,7 @@ __global__ __launch_bounds__(256) void fwd_branch_kernel(FwdBranchArgs a) {
         }
       }
       float m8[8];
-      ld8<float>(a.om, qh * DIM + d0, m8);
+      cvt8(mr[dc], m8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o8[e] = cm * m8[e] + cb * o8[e];
       st8<T>(OB, qh * DIM + d0, o8);
@@ -320,6 +365,18 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
   for (int it = 0; it < ITEMS; ++it)
 #pragma unroll
     for (int e = 0; e < 8; ++e) adk[it][e] = adv[it][e] = 0.f;
+  // each phase-2 item's key row and the range of its anchor's rows, fixed
+  // over the chunks
+  // (rows past the tile read the tile's last row; such items are skipped)
+  int it_lo[ITEMS], it_hi[ITEMS], it_an[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it)
+    it_an[it] = a.b_anchor[base + min((tid + 256 * it) / (DIM / 8), t.rows - 1)];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    it_lo[it] = a.branch_off[it_an[it]] - base;
+    it_hi[it] = a.branch_off[it_an[it] + 1] - base;
+  }
   const int nqv = t.rows * G;
   // phase 1: four threads per query vector of the chunk, each over a quarter of D
   const int ql = tid >> 2, sub = tid & 3;
@@ -338,6 +395,14 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
       const int nvis = a.bidir ? n : j + 1;
       const int kl0 = lo - base;
       const int64_t qh = int64_t(row) * a.hq + h;
+      Raw8<T> qr[QD / 8], dr[QD / 8];
+#pragma unroll
+      for (int dc = 0; dc < QD / 8; ++dc) {
+        qr[dc] = ldraw8<T>(QB, qh * DIM + sub * QD + dc * 8);
+        dr[dc] = ldraw8<T>(DOB, qh * DIM + sub * QD + dc * 8);
+      }
+      const float lse2 = a.lseb[qh] * kLog2e;
+      const float ndel = a.ndelta_b[qh];
       float s[MAXB], dp[MAXB];
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) s[jj] = dp[jj] = 0.f;
@@ -345,8 +410,10 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
       for (int dc = 0; dc < QD / 8; ++dc) {
         const int d0 = sub * QD + dc * 8;
         float q8[8], d8[8];
-        ld8_keep<T>(QB, qh * DIM + d0, sQ + ql * DIM + d0, q8);
-        ld8_keep<T>(DOB, qh * DIM + d0, sDO + ql * DIM + d0, d8);
+        keep8(qr[dc], sQ + ql * DIM + d0);
+        keep8(dr[dc], sDO + ql * DIM + d0);
+        cvt8(qr[dc], q8);
+        cvt8(dr[dc], d8);
 #pragma unroll
         for (int jj = 0; jj < MAXB; ++jj) {
           if (jj < nvis) {
@@ -372,8 +439,6 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
         dp[jj] += __shfl_xor(dp[jj], 1, 4);
         dp[jj] += __shfl_xor(dp[jj], 2, 4);
       }
-      const float lse2 = a.lseb[qh] * kLog2e;
-      const float ndel = a.ndelta_b[qh];
 #pragma unroll
       for (int jj = 0; jj < MAXB; ++jj) {
         float p = 0.f, d = 0.f;
@@ -415,9 +480,7 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
       const int item = tid + 256 * it;
       if (item < t.rows * (DIM / 8)) {
         const int kl = item / (DIM / 8), d4 = item % (DIM / 8);
-        const int an = a.b_anchor[base + kl];
-        const int lo = a.branch_off[an] - base;
-        const int hi = a.branch_off[an + 1] - base;
+        const int lo = it_lo[it], hi = it_hi[it];
         const int q_lo = max(lo * G, c0), q_hi = min(hi * G, c0 + nq);
         // this key is entry kl - lo of its anchor's queries' P / dS rows
         for (int qv = q_lo; qv < q_hi; ++qv) {
@@ -444,16 +507,11 @@ __global__ __launch_bounds__(256) void bwd_branch_kernel(BwdBranchArgs a) {
     if (item < t.rows * (DIM / 8)) {
       const int kl = item / (DIM / 8), d4 = item % (DIM / 8);
       const int64_t off = (int64_t(base + kl) * a.hkv + t.g) * DIM + d4 * 8;
+      float k8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (sizeof(T) == 2) {
-          DKB[off + e] = f2bf(adk[it][e] * a.scale);
-          DVB[off + e] = f2bf(adv[it][e]);
-        } else {
-          DKB[off + e] = adk[it][e] * a.scale;
-          DVB[off + e] = adv[it][e];
-        }
-      }
+      for (int e = 0; e < 8; ++e) k8[e] = adk[it][e] * a.scale;
+      st8<T>(DKB, off, k8);
+      st8<T>(DVB, off, adv[it]);
     }
   }
 }
