@@ -241,8 +241,9 @@ def main():
                          "forward; the metric and peak change accordingly)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU ring is not part of this build).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the "
+              "library computes one context-parallel rank's share on one GPU, with the other "
+              "ranks' K/V shards resident in its memory.", file=sys.stderr)
         sys.exit(2)
 
     import torch

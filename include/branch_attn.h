@@ -71,7 +71,7 @@ extern "C" {
 typedef enum {
   BA_OK = 0,
   BA_E_INVALID = 1,     /* bad argument (sizes, order, pointers, state) */
-  BA_E_UNSUPPORTED = 2, /* valid but outside what this build supports */
+  BA_E_UNSUPPORTED = 2, /* valid but outside what the library supports */
   BA_E_WORKSPACE = 3,   /* workspace missing or smaller than required */
   BA_E_HIP = 4,         /* a HIP runtime call or kernel launch failed */
   BA_E_OOM = 5          /* host or device allocation failed */
