@@ -513,7 +513,9 @@ extern "C" ba_status ba_qkv_project(const ba_plan *p, const ba_proj_args *a, voi
     if (a->target != 0 && a->target != 1) return fail(BA_E_INVALID, "target must be 0 or 1");
     if (a->hidden < 64 || a->hidden % 64 != 0)
       return fail(BA_E_INVALID, "hidden must be a positive multiple of 64");
-    if (int64_t(a->hidden) * 256 > (int64_t(1) << 31))
+    // a 256-row tile of x (2 bytes per element) must stay below 4 GiB: the
+    // tile loads address it with 32-bit offsets
+    if (int64_t(a->hidden) * 2 * 256 >= (int64_t(1) << 32))
       return fail(BA_E_UNSUPPORTED, "hidden too large for 32-bit tile offsets");
     if (!std::isfinite(a->rope_theta) || !std::isfinite(a->norm_eps) || a->norm_eps < 0.f)
       return fail(BA_E_INVALID, "rope_theta must be finite and norm_eps finite and >= 0");

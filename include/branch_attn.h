@@ -276,7 +276,9 @@ ba_status branch_attn_bwd(const ba_plan *plan, const ba_bwd_args *args, void *st
  *   w [(hq + 2 hkv) d, hidden]: q heads, then k heads, then v heads.
  *   q_norm, k_norm [d], both or neither.
  * Needs a bf16 plan with d == 128 (BA_E_UNSUPPORTED otherwise), hidden a
- * positive multiple of 64. Enqueue only; allocates nothing.
+ * positive multiple of 64 (BA_E_INVALID otherwise) and below 2^23
+ * (BA_E_UNSUPPORTED). Rows of the output tensors not listed above are not
+ * touched. Enqueue only; allocates nothing.
  */
 typedef struct {
   int32_t target;     /* 0: main rows, 1: branch rows */
