@@ -237,8 +237,8 @@ def main():
     ap.add_argument("--walk", default="auto", choices=["auto", "segments", "runs"],
                     help="key walk of the forward and dQ kernels (auto: chosen by chunk size)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"],
-                    help="fp8: Q/K/Qb/Kb as fp8 E4M3, V bf16, forward only (a step is the "
-                         "forward; the metric and peak change accordingly)")
+                    help="fp8: Q/K/Qb/Kb as fp8 E4M3, V bf16; a step is the forward "
+                         "(the metric and peak change accordingly)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the "
@@ -262,7 +262,9 @@ def main():
             sys.exit(2)
         w = dataclasses.replace(w, name=f"ttt{args.tokens}", seqlens=[args.tokens])
     fp8 = args.dtype == "fp8"
-    # a step is fwd+bwd for bf16 (every workload); the fp8 path is forward only
+    # a step is fwd+bwd for bf16 (every workload); for fp8 the step is the
+    # forward (the fp8 backward runs the bf16 kernels on exact bf16 copies of
+    # q, k, qb, kb, so the fp8 gain is the forward's)
     w = dataclasses.replace(w, dtype="fp8", bwd=False) if fp8 else dataclasses.replace(w, bwd=True)
     plan = ba.Plan(w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.anchors, w.branch_lens,
                    w.hq, w.hkv, w.d, w.dtype).upload()

@@ -15,7 +15,8 @@ Tensor layouts are those of the header: q/o [N, hq, d]; k/v [C, N, hkv, d]
 (shard s = rank s's local rows); qb/ob [NB, hq, d]; kb/vb [NB, hkv, d];
 lse [N, hq], lseb [NB, hq] float32. Element types: dtype "bf16" (bf16
 throughout), "fp32" (float32 throughout) or "fp8" (q, k, qb, kb as
-torch.float8_e4m3fn, i.e. OCP fp8 E4M3; v, vb, o, ob bf16; forward only).
+torch.float8_e4m3fn, i.e. OCP fp8 E4M3; v, vb, o, ob bf16; the backward
+returns bf16 gradients).
 """
 
 import ctypes
@@ -362,20 +363,22 @@ def fwd_static(plan, q, k, v, qb=None, kb=None, vb=None, out=None, scale=0.0):
 
 
 def bwd(plan, q, k, v, qb, kb, vb, o, lse, ob, lseb, do, dob, scale=0.0, workspace=None):
-    """Backward; returns (dq, dk, dv, dqb, dkb, dvb)."""
+    """Backward; returns (dq, dk, dv, dqb, dkb, dvb). For fp8 plans the
+    gradients are bf16."""
     torch = _torch()
     dev = q.device
-    dt = _tdtype(plan)
+    dt, qt = _tdtype(plan), _qkdtype(plan)
     S = _shapes(plan)
     nb = plan.info["n_branch_rows"]
-    for name, t, shp in (("q", q, S["q"]), ("k", k, S["k"]), ("v", v, S["k"]), ("o", o, S["q"]),
-                         ("do", do, S["q"])):
-        _expect(name, t, shp, dt, dev)
+    for name, t, shp, ty in (("q", q, S["q"], qt), ("k", k, S["k"], qt), ("v", v, S["k"], dt),
+                             ("o", o, S["q"], dt), ("do", do, S["q"], dt)):
+        _expect(name, t, shp, ty, dev)
     _expect("lse", lse, S["lse"], torch.float32, dev)
     if nb:
-        for name, t, shp in (("qb", qb, S["qb"]), ("kb", kb, S["kb"]), ("vb", vb, S["kb"]),
-                             ("ob", ob, S["qb"]), ("dob", dob, S["qb"])):
-            _expect(name, t, shp, dt, dev)
+        for name, t, shp, ty in (("qb", qb, S["qb"], qt), ("kb", kb, S["kb"], qt),
+                                 ("vb", vb, S["kb"], dt), ("ob", ob, S["qb"], dt),
+                                 ("dob", dob, S["qb"], dt)):
+            _expect(name, t, shp, ty, dev)
         _expect("lseb", lseb, S["lseb"], torch.float32, dev)
     dq = torch.empty(S["q"], dtype=dt, device=dev)
     dk = torch.empty(S["k"], dtype=dt, device=dev)

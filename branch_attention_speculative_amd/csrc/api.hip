@@ -359,8 +359,6 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
   try {
     ba_status st = check_plan(p);
     if (st != BA_OK) return st;
-    if (p->dtype == BA_FP8)
-      return fail(BA_E_UNSUPPORTED, "the fp8 path is forward only (no backward for fp8 inputs)");
     if (a == nullptr) return fail(BA_E_INVALID, "args is NULL");
     if (!a->q || !a->k || !a->v || !a->o || !a->lse || !a->dout || !a->dq || !a->dk || !a->dv)
       return fail(BA_E_INVALID, "q, k, v, o, lse, dout, dq, dk and dv are required");
@@ -385,6 +383,38 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     float *lse2 = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + del_bytes);
     float *dq_local = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + 2 * del_bytes);
 
+    // fp8 plans: the E4M3 q, k, qb, kb are converted to bf16 (exactly) into
+    // the workspace, and the bf16 backward runs on those copies
+    const void *Q = a->q, *K = a->k, *QB = a->qb, *KB = a->kb;
+    const int cdt = p->dtype == BA_FP8 ? int(BA_BF16) : p->dtype;
+    if (p->dtype == BA_FP8) {
+      auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+      char *c = static_cast<char *>(a->workspace) + 2 * del_bytes +
+                al(size_t(p->n_branch) * p->hq * p->d * 4);
+      const size_t nq = size_t(p->n_local) * p->hq * p->d, nk = size_t(p->C) * p->n_local * p->hkv * p->d;
+      const size_t nqb = size_t(p->n_branch) * p->hq * p->d, nkb = size_t(p->n_branch) * p->hkv * p->d;
+      uint16_t *q16 = reinterpret_cast<uint16_t *>(c);
+      uint16_t *k16 = reinterpret_cast<uint16_t *>(c + al(nq * 2));
+      uint16_t *qb16 = reinterpret_cast<uint16_t *>(c + al(nq * 2) + al(nk * 2));
+      uint16_t *kb16 = reinterpret_cast<uint16_t *>(c + al(nq * 2) + al(nk * 2) + al(nqb * 2));
+      struct Cv {
+        const void *src;
+        uint16_t *dst;
+        size_t n;
+      };
+      for (const Cv &cv : {Cv{a->q, q16, nq}, Cv{a->k, k16, nk}, Cv{a->qb, qb16, has_b ? nqb : 0},
+                           Cv{a->kb, kb16, has_b ? nkb : 0}}) {
+        hipError_t ce = timed("fp8_to_bf16", s, [&] {
+          return ba::launch_fp8_to_bf16(static_cast<const uint8_t *>(cv.src), cv.dst, int64_t(cv.n), s);
+        });
+        if (ce != hipSuccess) return hip_fail("fp8_to_bf16 launch", ce);
+      }
+      Q = q16;
+      K = k16;
+      QB = has_b ? qb16 : nullptr;
+      KB = has_b ? kb16 : nullptr;
+    }
+
     ba::BwdPreArgs pa{};
     pa.o = a->o;
     pa.ob = a->ob;
@@ -399,13 +429,13 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     pa.n_branch = int32_t(p->n_branch);
     pa.hq = p->hq;
     pa.d = p->d;
-    hipError_t e = timed("bwd_pre", s, [&] { return ba::launch_bwd_pre(pa, p->dtype, s); });
+    hipError_t e = timed("bwd_pre", s, [&] { return ba::launch_bwd_pre(pa, cdt, s); });
     if (e != hipSuccess) return hip_fail("bwd_pre launch", e);
 
     if (has_b) {
       ba::BwdBranchArgs b{};
-      b.qb = a->qb;
-      b.kb = a->kb;
+      b.qb = QB;
+      b.kb = KB;
       b.vb = a->vb;
       b.doutb = a->doutb;
       b.lseb = a->lseb;
@@ -424,15 +454,15 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
       b.scale = scale;
       b.scale_log2 = scale * ba::kLog2eHost;
       e = timed("bwd_branch", s, [&] {
-        return ba::launch_bwd_branch(b, int(p->btiles.size()), p->dtype, p->max_branch_len, s);
+        return ba::launch_bwd_branch(b, int(p->btiles.size()), cdt, p->max_branch_len, s);
       });
       if (e != hipSuccess) return hip_fail("bwd_branch launch", e);
     }
 
     ba::BwdDqArgs q{};
-    q.q = a->q;
-    q.qb = a->qb;
-    q.k = a->k;
+    q.q = Q;
+    q.qb = QB;
+    q.k = K;
     q.v = a->v;
     q.dout = a->dout;
     q.doutb = a->doutb;
@@ -460,9 +490,9 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     q.runs = ba::uses_run_walk(*p) ? 1 : 0;
 
     ba::BwdDkdvArgs k{};
-    k.q = a->q;
-    k.qb = a->qb;
-    k.k = a->k;
+    k.q = Q;
+    k.qb = QB;
+    k.k = K;
     k.v = a->v;
     k.dout = a->dout;
     k.doutb = a->doutb;
@@ -485,7 +515,7 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     k.scale = scale;
     k.scale_log2 = scale * ba::kLog2eHost;
 
-    if (p->dtype == BA_BF16) {
+    if (cdt == BA_BF16) {
       e = timed("bwd_dq", s, [&] { return ba::launch_bwd_dq_bf16(q, int(p->qtiles.size()), s); });
       if (e != hipSuccess) return hip_fail("bwd_dq launch", e);
       e = timed("bwd_dkdv", s, [&] { return ba::launch_bwd_dkdv_bf16(k, int(p->ktiles.size()), s); });

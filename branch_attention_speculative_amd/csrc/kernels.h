@@ -115,6 +115,8 @@ hipError_t launch_fwd_ring_bf16(const FwdRingArgs &a, int n_tiles, hipStream_t s
 hipError_t launch_fwd_ring_fp8(const FwdRingArgs &a, int n_tiles, hipStream_t s);
 hipError_t launch_fwd_branch(const FwdBranchArgs &a, int n_tiles, int dtype, int maxb, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdPreArgs &a, int dtype, hipStream_t s);
+// E4M3 codes -> bf16 (exact), n a multiple of 8
+hipError_t launch_fp8_to_bf16(const uint8_t *in, uint16_t *out, int64_t n, hipStream_t s);
 hipError_t launch_bwd_branch(const BwdBranchArgs &a, int n_tiles, int dtype, int maxb, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const BwdDqArgs &a, int n_tiles, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16(const BwdDkdvArgs &a, int n_tiles, hipStream_t s);

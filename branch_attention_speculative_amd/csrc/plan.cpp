@@ -41,9 +41,16 @@ size_t ws_fwd_bytes(const ba_plan &p) {
 
 // Backward workspace: Delta and LSE * log2(e) of every row (main then
 // branch, fp32) and the branch-local share of dQ of every branch row (fp32).
+// fp8 plans add bf16 copies of q, k, qb and kb, in that order (every E4M3
+// value is a bf16 value, so the backward runs on those copies).
 size_t ws_bwd_bytes(const ba_plan &p) {
-  return 2 * align256(size_t(p.n_local + p.n_branch) * p.hq * 4) +
-         align256(size_t(p.n_branch) * p.hq * p.d * 4);
+  size_t b = 2 * align256(size_t(p.n_local + p.n_branch) * p.hq * 4) +
+             align256(size_t(p.n_branch) * p.hq * p.d * 4);
+  if (p.dtype == BA_FP8)
+    b += align256(size_t(p.n_local) * p.hq * p.d * 2) +
+         align256(size_t(p.C) * p.n_local * p.hkv * p.d * 2) +
+         align256(size_t(p.n_branch) * p.hq * p.d * 2) + align256(size_t(p.n_branch) * p.hkv * p.d * 2);
+  return b;
 }
 
 // Order tiles for an XCD-round-robin dispatch: tiles arrive in locality order

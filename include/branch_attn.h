@@ -79,10 +79,13 @@ typedef enum {
 
 /* Element types. BA_FP8: q, k, qb, kb hold OCP fp8 E4M3 codes (1 byte:
  * exponent bias 7, no infinities, 0x7F/0xFF NaN); v, vb, o, ob are bf16; lse
- * fp32. The scores are then formed by fp8 matrix-core products with fp32
+ * fp32. The forward forms the scores by fp8 matrix-core products with fp32
  * accumulation, everything after them as for BA_BF16. Per-tensor fp8 scale
- * factors of Q and K fold into the softmax scale (s = scale * <q, k>).
- * Forward only: branch_attn_bwd returns BA_E_UNSUPPORTED for such a plan. */
+ * factors of Q and K fold into the softmax scale (s = scale * <q, k>). The
+ * backward takes the E4M3 values of q, k, qb, kb as bf16 (each E4M3 value is
+ * a bf16 value; the copies live in the backward workspace) and runs the bf16
+ * backward: dq, dk, dqb, dkb are bf16 gradients with respect to those
+ * values. */
 typedef enum { BA_BF16 = 0, BA_FP32 = 1, BA_FP8 = 2 } ba_dtype;
 
 typedef enum {

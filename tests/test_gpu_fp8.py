@@ -1,12 +1,13 @@
-"""GPU parity of the fp8 forward (dtype "fp8": Q, K, Qb, Kb as OCP fp8 E4M3
+"""GPU parity of the fp8 path (dtype "fp8": Q, K, Qb, Kb as OCP fp8 E4M3
 codes, V, Vb, O, Ob bf16) through the C ABI, against the oracle fed the same
 decoded fp8 values. The pages name fp8 as a precision to watch for the
 online-softmax merge (rainbus analysis, weaknesses and improvements, item 4);
 the tolerances are the bf16 ones: O max-abs <= 2e-2 and rel-L2 <= 1e-2, LSE
-max-abs <= 1e-3. The inputs are the bf16 workloads' seeded N(0, 1) draws,
-encoded to E4M3 for the score operands."""
+max-abs <= 1e-3, gradients as for bf16 inputs. The backward takes the E4M3
+values as bf16 and runs the bf16 backward, which one test checks bit for bit
+against the bf16 plan on the decoded values. The inputs are the bf16
+workloads' seeded N(0, 1) draws, encoded to E4M3 for the score operands."""
 
-import ctypes
 
 import numpy as np
 import pytest
@@ -14,8 +15,8 @@ import pytest
 import workloads
 from oracle import pack
 
-from helpers import LazyF32, inputs, lse_err, make_plan, max_abs, oracle_grouped, oracle_structs, \
-    rel_l2, say, subset_grouped, to_device, to_host
+from helpers import LazyF32, grad_ok, inputs, lse_err, make_plan, max_abs, oracle_grouped, \
+    oracle_structs, rel_l2, say, subset_grouped, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -115,12 +116,50 @@ def test_fp8_forward_full_size_long256k_sampled(env):
     _check("ob", to_host(ob[bi]), ref["ob"], to_host(lseb[bi]), ref["lseb"])
 
 
-def test_fp8_backward_is_rejected(env):
+@pytest.mark.parametrize("name", ["ttt32k_r", "dflash_r", "dspark_r"])
+def test_fp8_backward_matches_the_oracle(env, name):
+    """Forward and backward on an fp8 plan against the oracle's dense
+    backward on the decoded values (the gradients are bf16)."""
     torch, ba = env
-    w = _fp8(workloads.make("dflash_r"))
+    w = _fp8(workloads.make(name))
+    say(f"[case] fp8 backward {w.name}")
+    lay, br = oracle_structs(w)
     plan = make_plan(ba, w)
-    args = ba.BwdArgs(scale=0.0)
-    L = ba.lib()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    assert L.branch_attn_bwd(plan.handle, ctypes.byref(args), stream) == 2  # BA_E_UNSUPPORTED
-    assert b"forward only" in L.ba_last_error()
+    N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
+    raw, dec = inputs(w, N, NB)
+    dev = {k: to_device(torch, w, v) for k, v in raw.items()}
+    o, lse, ob, lseb = ba.fwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+    g = ba.bwd(plan, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"], o, lse, ob, lseb,
+               dev["do"], dev["dob"])
+    torch.cuda.synchronize()
+    assert all(t is None or t.dtype == torch.bfloat16 for t in g)
+    ref = oracle_grouped(lay, br, *(dec[k] for k in ("q", "k", "v", "qb", "kb", "vb")), dec["do"],
+                         dec["dob"])
+    for nm, t in zip(("dq", "dk", "dv", "dqb", "dkb", "dvb"), g):
+        got = to_host(t) if t is not None else np.zeros(0)
+        ok, ma, rl = grad_ok(got, ref[nm], True)
+        say(f"  {nm}: max-abs={ma:.3e} relL2={rl:.3e}")
+        assert ok, (nm, ma, rl)
+
+
+def test_fp8_backward_equals_the_bf16_backward_on_decoded_values(env):
+    """Every E4M3 value is a bf16 value: the fp8 plan's backward and the bf16
+    plan's backward on q, k, qb, kb decoded to bf16 (same O, LSE and dO) give
+    identical gradients."""
+    torch, ba = env
+    w8 = _fp8(workloads.make("long256k_r"))
+    w16 = workloads.make("long256k_r")
+    p8, p16 = make_plan(ba, w8), make_plan(ba, w16)
+    N, NB = p8.info["n_local_rows"], p8.info["n_branch_rows"]
+    raw, _ = inputs(w8, N, NB)
+    dev = {k: to_device(torch, w8, v) for k, v in raw.items()}
+    o, lse, ob, lseb = ba.fwd(p8, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"])
+    as16 = {k: dev[k].to(torch.bfloat16) for k in ("q", "k", "qb", "kb")}
+    g8 = ba.bwd(p8, dev["q"], dev["k"], dev["v"], dev["qb"], dev["kb"], dev["vb"], o, lse, ob, lseb,
+                dev["do"], dev["dob"])
+    g16 = ba.bwd(p16, as16["q"], as16["k"], dev["v"], as16["qb"], as16["kb"], dev["vb"], o, lse, ob,
+                 lseb, dev["do"], dev["dob"])
+    torch.cuda.synchronize()
+    for nm, a, b in zip(("dq", "dk", "dv", "dqb", "dkb", "dvb"), g8, g16):
+        assert torch.equal(a, b), nm
+    say(f"  fp8 and bf16 backward bit-identical on {N} rows + {NB} branch rows")
