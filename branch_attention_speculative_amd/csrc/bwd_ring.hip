@@ -450,6 +450,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   dma_wait();
   // The two roles run separate loops with the same barrier sequence.
   if (role == 0) {
+    // The dV wave is the one its partner waits for at the barrier: it issues
+    // first when both have an instruction ready (0.26% faster on long256k;
+    // the opposite priority is 5% slower).
+    __builtin_amdgcn_s_setprio(1);
     // block b in the set (Qc, Dc, Lc, Bc); block b + 1 loads into the next set
     auto iter = [&](int b, const u16 *Qc, const u16 *Dc, const float *Lc, const int *Bc, uint32_t *Xc,
                     u16 *Qn, u16 *Dn, float *Ln, float *En, int *Bn) {
