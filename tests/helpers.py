@@ -130,6 +130,32 @@ def shift_late_keys(lam):
     return prep
 
 
+def random_workload(seed, dtype="bf16"):
+    """A seeded random small workload: the branch kinds in turn, C from 1 to
+    16 and any rank, one to five sequences of 1..1200 tokens, GQA groups of 1
+    to 16 over 1 to 4 kv-heads, TTT depths 1..8, block anchors anywhere in the
+    packed stream with block lengths 1..64. The fp8 form has no backward
+    flag (its tests call the backward themselves)."""
+    rng = np.random.default_rng(7000 + seed)
+    kind = [pack.KIND_NONE, pack.KIND_TTT, pack.KIND_BLOCK_BIDIR, pack.KIND_BLOCK_CAUSAL][seed % 4]
+    C = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    r = int(rng.integers(0, C))
+    lens = [int(x) for x in rng.integers(1, 1201, size=int(rng.integers(1, 6)))]
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8, 16]))
+    depth, anchors, blens = 0, None, None
+    if kind == pack.KIND_TTT:
+        depth = int(rng.integers(1, 9))
+    elif kind != pack.KIND_NONE:
+        total = sum(lens)
+        n_a = int(rng.integers(1, min(total, 24) + 1))
+        anchors = sorted(int(x) for x in rng.choice(total, size=n_a, replace=False))
+        blens = [int(x) for x in rng.integers(1, 65, size=n_a)]
+    name = f"random-{seed}"
+    return workloads.Workload(name, lens, C, r, kind, depth, hq, hkv, 128, dtype, dtype == "bf16",
+                              sum(ord(ch) for ch in name), anchors=anchors, branch_lens=blens)
+
+
 def oracle_grouped(lay, br, q, k, v, qb, kb, vb, do=None, dob=None, dtype=np.float32,
                    threads=4, log=None):
     """The oracle's dense forward (and with do/dob its backward), evaluated one

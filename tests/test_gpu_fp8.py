@@ -16,7 +16,7 @@ import workloads
 from oracle import pack
 
 from helpers import LazyF32, grad_ok, inputs, lse_err, make_plan, max_abs, oracle_grouped, \
-    oracle_structs, rel_l2, say, subset_grouped, to_device, to_host
+    oracle_structs, random_workload, rel_l2, say, subset_grouped, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -121,9 +121,23 @@ def test_fp8_forward_full_size_long256k_sampled(env):
 def test_fp8_backward_matches_the_oracle(env, name):
     """Forward and backward on an fp8 plan against the oracle's dense
     backward on the decoded values (the gradients are bf16)."""
+    _fwd_bwd_against_oracle(env, _fp8(workloads.make(name)))
+
+
+FP8_RANDOM = [random_workload(i, "fp8") for i in range(8)]
+
+
+@pytest.mark.parametrize("w", FP8_RANDOM, ids=[w.name for w in FP8_RANDOM])
+def test_fp8_random_configurations(env, w):
+    """Seeded random shapes (every branch kind, C up to 16, GQA groups up to
+    16): the fp8 forward and backward against the oracle."""
+    _fwd_bwd_against_oracle(env, w)
+
+
+def _fwd_bwd_against_oracle(env, w):
     torch, ba = env
-    w = _fp8(workloads.make(name))
-    say(f"[case] fp8 backward {w.name}")
+    say(f"[case] fp8 fwd+bwd {w.name}: lens={w.seqlens[:6]} C={w.C} r={w.r} kind={w.kind} "
+        f"heads={w.hq}/{w.hkv}")
     lay, br = oracle_structs(w)
     plan = make_plan(ba, w)
     N, NB = plan.info["n_local_rows"], plan.info["n_branch_rows"]
@@ -136,6 +150,9 @@ def test_fp8_backward_matches_the_oracle(env, name):
     assert all(t is None or t.dtype == torch.bfloat16 for t in g)
     ref = oracle_grouped(lay, br, *(dec[k] for k in ("q", "k", "v", "qb", "kb", "vb")), dec["do"],
                          dec["dob"])
+    _check("o", to_host(o), ref["o"], to_host(lse), ref["lse"])
+    if NB:
+        _check("ob", to_host(ob), ref["ob"], to_host(lseb), ref["lseb"])
     for nm, t in zip(("dq", "dk", "dv", "dqb", "dkb", "dvb"), g):
         got = to_host(t) if t is not None else np.zeros(0)
         ok, ma, rl = grad_ok(got, ref[nm], True)

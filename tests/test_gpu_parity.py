@@ -20,7 +20,8 @@ import workloads
 from oracle import attn, pack
 
 from helpers import LazyF32, complete_keys, grad_ok, inputs, lse_err, make_plan, max_abs, \
-    oracle_grouped, oracle_structs, rel_l2, say, shift_late_keys, subset_grouped, to_device, to_host
+    oracle_grouped, oracle_structs, random_workload, rel_l2, say, shift_late_keys, subset_grouped, \
+    to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -189,30 +190,7 @@ def test_edge_cases(env, w):
     _check_bwd(w, got, ref)
 
 
-def _random_case(seed):
-    """A seeded random small workload: the branch kinds in turn, C from 1 to
-    16 and any rank, one to five sequences of 1..1200 tokens, GQA groups of 1
-    to 16 over 1 to 4 kv-heads, TTT depths 1..8, block anchors anywhere in the
-    packed stream with block lengths 1..64."""
-    rng = np.random.default_rng(7000 + seed)
-    kind = [pack.KIND_NONE, pack.KIND_TTT, pack.KIND_BLOCK_BIDIR, pack.KIND_BLOCK_CAUSAL][seed % 4]
-    C = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
-    r = int(rng.integers(0, C))
-    lens = [int(x) for x in rng.integers(1, 1201, size=int(rng.integers(1, 6)))]
-    hkv = int(rng.choice([1, 2, 4]))
-    hq = hkv * int(rng.choice([1, 2, 4, 8, 16]))
-    depth, anchors, blens = 0, None, None
-    if kind == pack.KIND_TTT:
-        depth = int(rng.integers(1, 9))
-    elif kind != pack.KIND_NONE:
-        total = sum(lens)
-        n_a = int(rng.integers(1, min(total, 24) + 1))
-        anchors = sorted(int(x) for x in rng.choice(total, size=n_a, replace=False))
-        blens = [int(x) for x in rng.integers(1, 65, size=n_a)]
-    return _edge(f"random-{seed}", lens, C, r, kind, depth, hq, hkv, anchors, blens)
-
-
-RANDOM_CASES = [_random_case(i) for i in range(16)]
+RANDOM_CASES = [random_workload(i) for i in range(16)]
 
 
 @pytest.mark.parametrize("w", RANDOM_CASES, ids=[e.name for e in RANDOM_CASES])
