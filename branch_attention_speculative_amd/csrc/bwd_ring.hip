@@ -220,23 +220,36 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
 
 constexpr int kQB = 64;  // query vectors per inner block
 
-// Inner blocks are numbered over the main-row range then the branch-row range.
+// Inner blocks are numbered over the branch-row range, then the main-row
+// range, each walked from its end backwards in blocks that end on a multiple
+// of RB rows from the range end (the partial block, which holds the range's
+// first rows, comes last). Every key tile of a kv-head ends its ranges on
+// the same rows, so the tiles that start together on an XCD read the same
+// Q / dO rows at about the same time and share them in L2: on the long
+// workload this halves the kernel's HBM reads against walking forward from
+// each tile's own first row.
 struct QBlock {
   int src, r0, nr, hi;
 };
 
 __device__ __forceinline__ QBlock qblock(const KTile &t, int b, int RB, int nb_main) {
+  const int nb_branch = (t.qb_end - t.qb_start + RB - 1) / RB;
   QBlock q;
-  if (b < nb_main) {
-    q.src = 0;
-    q.r0 = t.qm_start + b * RB;
-    q.hi = t.qm_end;
-  } else {
+  int lo, end, k;
+  if (b < nb_branch) {
     q.src = 1;
-    q.r0 = t.qb_start + (b - nb_main) * RB;
-    q.hi = t.qb_end;
+    lo = t.qb_start;
+    end = t.qb_end;
+    k = b;
+  } else {
+    q.src = 0;
+    lo = t.qm_start;
+    end = t.qm_end;
+    k = b - nb_branch;
   }
-  q.nr = min(RB, q.hi - q.r0);
+  q.hi = end - k * RB;  // one past the block's last row
+  q.r0 = max(q.hi - RB, lo);
+  q.nr = q.hi - q.r0;
   return q;
 }
 
