@@ -190,7 +190,7 @@ def test_edge_cases(env, w):
     _check_bwd(w, got, ref)
 
 
-RANDOM_CASES = [random_workload(i) for i in range(16)]
+RANDOM_CASES = [random_workload(i) for i in range(64)]
 
 
 @pytest.mark.parametrize("w", RANDOM_CASES, ids=[e.name for e in RANDOM_CASES])
