@@ -124,7 +124,7 @@ def test_fp8_backward_matches_the_oracle(env, name):
     _fwd_bwd_against_oracle(env, _fp8(workloads.make(name)))
 
 
-FP8_RANDOM = [random_workload(i, "fp8") for i in range(8)]
+FP8_RANDOM = [random_workload(i, "fp8") for i in range(32)]
 
 
 @pytest.mark.parametrize("w", FP8_RANDOM, ids=[w.name for w in FP8_RANDOM])
