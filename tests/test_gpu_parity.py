@@ -202,6 +202,27 @@ def test_random_configurations(env, w):
     _check_bwd(w, got, ref)
 
 
+def _fp32_random(i):
+    w = random_workload(i, "fp32")
+    d = 64 if i % 2 else 128
+    return workloads.Workload(f"{w.name}-fp32-d{d}", w.seqlens, w.C, w.r, w.kind, w.depth_or_block,
+                              w.hq, w.hkv, d, "fp32", True, w.seed, anchors=w.anchors,
+                              branch_lens=w.branch_lens)
+
+
+FP32_RANDOM_CASES = [_fp32_random(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("w", FP32_RANDOM_CASES, ids=[e.name for e in FP32_RANDOM_CASES])
+def test_fp32_random_configurations(env, w):
+    """The same seeded random shapes in fp32 (the vector-unit path), d = 128
+    and 64 in turn: forward and backward element by element against the
+    oracle in float64, at the fp32 bounds."""
+    got, ref, _ = _run(env, w, with_bwd=True, oracle_dtype=np.float64)
+    _check_fwd(w, got, ref)
+    _check_bwd(w, got, ref)
+
+
 @pytest.mark.parametrize("walk", ["segments", "runs"])
 @pytest.mark.parametrize("name", ["ttt32k_r", "dspark_r", "long256k_r", "short-c8", "c64",
                                   "many-seqs", "ragged"])
