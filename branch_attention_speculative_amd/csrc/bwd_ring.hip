@@ -388,7 +388,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
   const int kk = (wave & 3) * 32 + qi;  // this lane's key inside the tile
   const bool kvalid = kk < t.nkeys;
   const int kpos = t.kpos0 + kk;
-  const int64_t krow = int64_t(t.shard) * a.n_local + t.krow0 + min(kk, t.nkeys - 1);
+  int64_t krow;
+  if (t.run > 0) {  // packed joined runs of consecutive shards
+    const int v = t.run_off + min(kk, t.nkeys - 1);
+    krow = int64_t(t.shard + v / t.run) * a.n_local + t.krow0 + v % t.run;
+  } else {
+    krow = int64_t(t.shard) * a.n_local + t.krow0 + min(kk, t.nkeys - 1);
+  }
   const int64_t koff = (krow * a.hkv + t.g) * 128;
   const int G = a.G, log2G = a.log2G;
   const float c = a.scale_log2;

@@ -297,13 +297,16 @@ static ba_status build(ba_plan &p, const int32_t *seqlens, const int32_t *anchor
         // spans the two chunks takes kpos0 = (its largest key position) -
         // (nkeys - 1): the in-kernel test kpos0 + kk <= bound then holds for
         // every key and every row in its range, as the true positions do.
-        auto emit = [&](int sh, int32_t row_off, int32_t nk, int32_t pos_first, int32_t pos_last) {
+        auto emit = [&](int sh, int32_t row_off, int32_t nk, int32_t pos_first, int32_t pos_last,
+                        int32_t run = 0, int32_t run_off = 0) {
           KTile t{};
           t.g = g;
           t.shard = sh;
           t.krow0 = base + row_off;
           t.nkeys = nk;
           t.kpos0 = pos_last - (nk - 1);
+          t.run = run;
+          t.run_off = run_off;
           // main rows with bound >= the smallest key position
           const int32_t qs = int32_t(
               std::lower_bound(p.pos.begin() + base, p.pos.begin() + real_end, pos_first) -
@@ -322,9 +325,39 @@ static ba_status build(ba_plan &p, const int32_t *seqlens, const int32_t *anchor
                            (double(t.qm_end - t.qm_start) + double(t.qb_end - t.qb_start)) +
                        1.0);
         };
+        // The joined shards are sh0 .. C-1 (the condition holds from some
+        // shard on). All of them are seen, in full, by the same rows (this
+        // rank's tail chunk and the anchors in it), so when there are two or
+        // more their runs are packed back to back into full tiles: key v of
+        // the packed sequence is row v % 2c of shard sh0 + v / 2c. With short
+        // chunks this removes most partial tiles, whose idle wave pairs
+        // leave a SIMD without work. Runs of kPackRunMaxKeys keys or more
+        // waste little in their one partial tile and stay unpacked.
+        int sh0 = C;
+        for (int sh = C - 1; sh > r && int64_t(2 * C - sh) * c <= p.L[s]; --sh) sh0 = sh;
+        const int n_joined = 2 * c < kPackRunMaxKeys ? C - sh0 : 0;
+        if (n_joined >= 2) {
+          const int32_t run = 2 * c;
+          auto pos_of = [&](int64_t v) {
+            const int sh = sh0 + int(v / run);
+            const int32_t i = int32_t(v % run);
+            return i < c ? sh * c + i : (2 * C - 1 - sh) * c + (i - c);
+          };
+          const int64_t total = int64_t(n_joined) * run;
+          for (int64_t v0 = 0; v0 < total; v0 += kKTileKeys) {
+            const int32_t nk = int32_t(std::min<int64_t>(kKTileKeys, total - v0));
+            int32_t pmin = INT32_MAX, pmax = INT32_MIN;
+            for (int64_t v = v0; v < v0 + nk; ++v) {
+              pmin = std::min(pmin, pos_of(v));
+              pmax = std::max(pmax, pos_of(v));
+            }
+            emit(sh0 + int(v0 / run), 0, nk, pmin, pmax, run, int32_t(v0 % run));
+          }
+        }
         for (int sh = 0; sh < C; ++sh) {
           const int32_t tail = 2 * C - 1 - sh;
           const bool joined = sh > r && int64_t(tail + 1) * c <= p.L[s];
+          if (joined && n_joined >= 2) continue;  // packed above
           if (joined) {
             // row i of the run: chunk sh for i < c, chunk tail after
             auto pos_of = [&](int32_t i) { return i < c ? sh * c + i : tail * c + (i - c); };

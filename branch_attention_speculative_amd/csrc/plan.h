@@ -13,6 +13,10 @@ namespace ba {
 // Tiling constants of the bf16 MFMA kernels (D = 128).
 constexpr int kQTileVecs = 256;   // query vectors (row, head) per forward / dQ tile
 constexpr int kKTileKeys = 128;   // keys per dK/dV tile
+// joined chunk pairs shorter than this are packed across shards into full
+// dK/dV tiles (dspark: dK/dV 12% faster; with runs of 1024-3072 keys, as in
+// ttt32k, packing saved 1% of the tiles and measured 1% slower)
+constexpr int kPackRunMaxKeys = 1024;
 constexpr int kKBlockVecs = 64;   // query vectors per dK/dV inner block
 constexpr int kMaxBranch = 64;    // longest branch the branch-local kernels accept
 constexpr int kNumXcd = 8;        // MI355X: 8 accelerator complex dies, WGs dispatched round-robin
@@ -34,17 +38,20 @@ struct QTile {
 };
 static_assert(sizeof(QTile) == 32, "QTile layout");
 
-// Key tile of the dK/dV kernel: up to kKTileKeys consecutive key rows of one
-// shard and one sequence, for one kv-head, plus the local query rows that can
-// see any of them (a suffix of the sequence's main rows, and of its branch
-// rows). The rows lie in one chunk, or span the shard's two chunks of the
-// sequence when every local row sees both chunks or neither; key kk is then
-// masked as if at position kpos0 + kk, which decides visibility exactly as
-// the true positions do.
+// Key tile of the dK/dV kernel: up to kKTileKeys key rows of one sequence,
+// for one kv-head, plus the local query rows that can see any of them (a
+// suffix of the sequence's main rows, and of its branch rows). With run == 0
+// the keys are consecutive rows krow0 .. of shard `shard`: they lie in one
+// chunk, or span the shard's two chunks of the sequence when every local row
+// sees both chunks or neither. With run > 0 the tile packs the joined chunk
+// pairs of consecutive shards, each run = 2c rows starting at row krow0 of
+// its shard: key kk is row krow0 + (run_off + kk) % run of shard
+// shard + (run_off + kk) / run. Key kk is masked as if at position
+// kpos0 + kk, which decides visibility exactly as the true positions do.
 struct KTile {
   int32_t g, shard, krow0, kpos0;
   int32_t nkeys, qm_start, qm_end, qb_start;
-  int32_t qb_end, seq, pad0, pad1;
+  int32_t qb_end, seq, run, run_off;
 };
 static_assert(sizeof(KTile) == 48, "KTile layout");
 

@@ -179,8 +179,12 @@ void ba_plan_destroy(ba_plan *plan); /* frees host and device memory; NULL is a 
  * kernels, 8 int32 each {kv_head, source (0 main rows, 1 branch rows), first
  * row, rows, first local row of the sequence, chunk size, smallest causal
  * bound, largest causal bound}; which = 1: key tiles of the dK/dV kernel, 12
- * int32 each {kv_head, shard, first key row in the shard, its position, keys,
- * first/end main row, first/end branch row, sequence, 0, 0}; which = 2:
+ * int32 each {kv_head, shard, first key row in the shard, the position the
+ * kernel's mask gives key 0, keys, first/end main row, first/end branch row,
+ * sequence, run, run offset}: with run = 0 the keys are consecutive rows of
+ * the shard; with run > 0 key k is row first + (offset + k) % run of shard
+ * shard + (offset + k) / run (the chunk pairs of consecutive shards, packed
+ * back to back); which = 2:
  * branch tiles, 4 int32 each {kv_head, first anchor, end anchor, rows}.
  * Tiles with zero rows/keys are padding slots. Order = launch order.
  */

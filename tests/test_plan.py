@@ -144,14 +144,26 @@ def _check_worklists(p, lay, br, w):
     seen_k = np.zeros((w.hkv, C, N), int)
     shard_pos = [pack.zigzag_layout(w.seqlens, C, sh)["pos"] for sh in range(C)]
     joined = 0
-    for g, sh, krow0, kpos0, nk, qm0, qm1, qb0, qb1, s, _, _ in kt:
+    packed = 0
+    for g, sh, krow0, kpos0, nk, qm0, qm1, qb0, qb1, s, run, run_off in kt:
         if nk == 0:
             continue
         assert nk <= 128
         lo, hi = lay["cu_local"][s], lay["cu_local"][s + 1]
-        assert lo <= krow0 and krow0 + nk <= hi
-        seen_k[g, sh, krow0:krow0 + nk] += 1
-        true_pos = shard_pos[sh][krow0:krow0 + nk]
+        if run == 0:  # consecutive rows of one shard
+            assert run_off == 0
+            shs = np.full(nk, sh)
+            rows = krow0 + np.arange(nk)
+        else:  # chunk pairs of consecutive shards packed back to back
+            assert run == 2 * lay["c"][s] and krow0 == lo and 0 <= run_off < run
+            v = run_off + np.arange(nk)
+            shs = sh + v // run
+            rows = krow0 + v % run
+            assert shs.max() < C
+            packed += 1
+        assert lo <= rows.min() and rows.max() < hi
+        np.add.at(seen_k, (g, shs, rows), 1)
+        true_pos = np.array([shard_pos[a][b] for a, b in zip(shs, rows)])
         kern_pos = kpos0 + np.arange(nk)
         joined += int(np.any(np.diff(true_pos) != 1))
         want = [i for i in range(lo, hi) if bound_m[i] >= true_pos.min()]
@@ -178,16 +190,16 @@ def _check_worklists(p, lay, br, w):
         assert rows == br["branch_off"][a1] - br["branch_off"][a0]
         assert rows <= 64 and (rows * G <= 128 or a1 - a0 == 1)
     assert np.all(seen_a == 1)
-    return joined
+    return joined, packed
 
 
 @pytest.mark.parametrize("name", ["tiny", "ttt32k_r", "dflash_r", "dspark_r", "long256k_r"])
 def test_worklists_cover_everything(name):
     w = workloads.make(name)
     p, lay, br = _compare(w)
-    joined = _check_worklists(p, lay, br, w)
-    if name in ("ttt32k_r", "dspark_r"):  # short chunks: key tiles span both chunks of a shard
-        assert joined > 0
+    joined, packed = _check_worklists(p, lay, br, w)
+    if name in ("ttt32k_r", "dspark_r"):  # short chunks: key tiles span chunks and shards
+        assert joined > 0 and packed > 0
 
 
 def test_xcd_interleave_keeps_kv_heads_together_on_the_long_workload():
