@@ -384,7 +384,8 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     float *dq_local = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + 2 * del_bytes);
 
     // fp8 plans: the E4M3 q, k, qb, kb are converted to bf16 (exactly) into
-    // the workspace, and the bf16 backward runs on those copies
+    // the workspace, and the bf16 backward runs on those copies, except for
+    // the dQ kernel's scores, which take the E4M3 originals
     const void *Q = a->q, *K = a->k, *QB = a->qb, *KB = a->kb;
     const int cdt = p->dtype == BA_FP8 ? int(BA_BF16) : p->dtype;
     if (p->dtype == BA_FP8) {
@@ -488,6 +489,11 @@ extern "C" ba_status branch_attn_bwd(const ba_plan *p, const ba_bwd_args *a, voi
     q.scale = scale;
     q.scale_log2 = scale * ba::kLog2eHost;
     q.runs = ba::uses_run_walk(*p) ? 1 : 0;
+    if (p->dtype == BA_FP8) {  // scores on the fp8 matrix cores from the E4M3 originals
+      q.q8 = a->q;
+      q.qb8 = has_b ? a->qb : nullptr;
+      q.k8 = a->k;
+    }
 
     ba::BwdDkdvArgs k{};
     k.q = Q;

@@ -36,17 +36,24 @@ constexpr int kBN = 64;  // keys per block in the dQ kernel
 // bound or the chunk's visible end (need_mask), scores of keys past lim (the
 // last visible key for this lane, relative to the block, minus 4 hf) are
 // set to -inf before the exponentials.
+template <bool QK8>
 __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[8],
-                                         const bf16x8 (&dreg)[8], const u16 *bk, const u16 *bv,
+                                         const i32x8 (&q8)[2], const bf16x8 (&dreg)[8],
+                                         const u16 *bk, const u16 *bk8, const u16 *bv,
                                          bool need_mask, int lim, float lse2, const f32x16 &ndelta,
-                                         float c, const NatOff &no, const TrOff &to) {
+                                         float c, const NatOff &no, const Nat8Off &no8,
+                                         const TrOff &to) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     // dP^T accumulates onto -Delta, so it comes out as dP - Delta
     f32x16 s = f32x16{}, p = ndelta;
+    if constexpr (QK8) {  // S^T from the E4M3 K tile and Q registers
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) s = mfma32_f8(lds_nat8(bk8, 32 * kt, kk, no8), q8[kk], s);
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s = mfma32(lds_nat_o(bk, 32 * kt, ks, no), qreg[ks], s);
+      if constexpr (!QK8) s = mfma32(lds_nat_o(bk, 32 * kt, ks, no), qreg[ks], s);
       p = mfma32(lds_nat_o(bv, 32 * kt, ks, no), dreg[ks], p);
     }
     if (need_mask) {
@@ -71,13 +78,19 @@ __device__ __forceinline__ void dq_block(f32x16 (&acc)[4], const bf16x8 (&qreg)[
 
 constexpr int kDqWaves = 8;  // waves per dQ workgroup (32 query vectors each)
 
-// RUNS: walk the tile's run list (else the segments)
-template <bool RUNS>
+// RUNS: walk the tile's run list (else the segments). QK8: the scores come
+// from the fp8 matrix cores on the E4M3 Q and K (an fp8 plan), which halves
+// their share of the matrix-core time; K^T dS^T still takes the exact bf16
+// copy of K.
+template <bool RUNS, bool QK8>
 __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sK0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sV0[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sK1[kBN * kRS];
   __shared__ __attribute__((aligned(16))) u16 sV1[kBN * kRS];
+  // E4M3 K tiles: 64 rows of 128 bytes
+  __shared__ __attribute__((aligned(16))) u16 sK80[QK8 ? kBN * 64 : 8];
+  __shared__ __attribute__((aligned(16))) u16 sK81[QK8 ? kBN * 64 : 8];
   __shared__ __attribute__((aligned(16))) RunSeg sRuns[RUNS ? kMaxRuns : 1];
   __shared__ int sNRuns;
 
@@ -102,13 +115,26 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
   const float ndel = (bound >= 0) ? a.ndelta[qall] : 0.f;
 
   bf16x8 qreg[8], dreg[8];
+  i32x8 q8[2];
   {
     const u16 *qp = Q + qh * 128 + hf * 8;
     const u16 *dp = DO + qh * 128 + hf * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      qreg[ks] = as_bf16x8(valid ? *reinterpret_cast<const u32x4 *>(qp + ks * 16) : u32x4{0, 0, 0, 0});
+      if constexpr (!QK8)
+        qreg[ks] = as_bf16x8(valid ? *reinterpret_cast<const u32x4 *>(qp + ks * 16) : u32x4{0, 0, 0, 0});
       dreg[ks] = as_bf16x8(valid ? *reinterpret_cast<const u32x4 *>(dp + ks * 16) : u32x4{0, 0, 0, 0});
+    }
+    if constexpr (QK8) {
+      // E4M3 rows are 128 bytes: this lane's bytes 64 kk + 32 hf .. + 31
+      const char *q8p = static_cast<const char *>(t.src ? a.qb8 : a.q8) + qh * 128 + hf * 32;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 lo = valid ? *reinterpret_cast<const u32x4 *>(q8p + 64 * kk) : u32x4{0, 0, 0, 0};
+        const u32x4 hi = valid ? *reinterpret_cast<const u32x4 *>(q8p + 64 * kk + 16) : u32x4{0, 0, 0, 0};
+        q8[kk] = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+                       int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+      }
     }
   }
   f32x16 acc[4];
@@ -119,16 +145,23 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
   const int g = t.g;
 
   const NatOff no = nat_offsets(lane);
+  const Nat8Off no8 = nat8_offsets(lane);
   const TrOff to = tr_offsets(lane);
   const DmaOff<kDqWaves> dof =
       dma_offsets<kDqWaves>(wave, lane, [&](int r) { return int64_t(r) * rs; });
+  // E4M3 K: rows of hkv * 128 bytes
+  const uint32_t dof8 = dma8_offset(wave, lane, rs);
+  const char *K8 = static_cast<const char *>(a.k8);
   // K/V rows j0 .. j0 + 63 of a chunk; rows past the chunk's visible end
   // are not read (their P is masked to zero)
-  auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv) {
+  auto dma_kv = [&](const Seg &s, int j0, u16 *dk, u16 *dv, u16 *dk8) {
     const int64_t off = (s.krow + j0) * rs + g * 128;
     const uint32_t bytes = uint32_t(((min(kBN, s.n_hi - j0) - 1) * rs + 128) * 2);
     dma_tile64_buf<kDqWaves>(dk, buf_rsrc(K + off, bytes), dof, wave);
     dma_tile64_buf<kDqWaves>(dv, buf_rsrc(V + off, bytes), dof, wave);
+    // same rows at one byte per element: the element offset is the byte
+    // offset, and the extent is half the bf16 one
+    if constexpr (QK8) dma_tile64_f8(dk8, buf_rsrc(K8 + off, bytes / 2), dof8, wave);
   };
   f32x16 ndelta;
 #pragma unroll
@@ -138,6 +171,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
   lds_zero(sV0, kBN * kRS, tid, kDqWaves * 64);
   lds_zero(sK1, kBN * kRS, tid, kDqWaves * 64);
   lds_zero(sV1, kBN * kRS, tid, kDqWaves * 64);
+  if constexpr (QK8) {
+    lds_zero(sK80, kBN * 64, tid, kDqWaves * 64);
+    lds_zero(sK81, kBN * 64, tid, kDqWaves * 64);
+  }
   if constexpr (RUNS) {
     if (wave == 0) build_runs(sRuns, &sNRuns, t, a.C, a.r, a.n_local, lane);
   }
@@ -158,7 +195,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
     else
       next_block<kBN>(sg, j0, s, t, a.C, a.r, a.n_local);
   };
-  if (sg < nseg) dma_kv(s, j0, sK0, sV0);
+  if (sg < nseg) dma_kv(s, j0, sK0, sV0, sK80);
   dma_wait();
   __syncthreads();
   while (sg < nseg) {
@@ -166,11 +203,11 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
       const Seg cs = s;
       const int cj0 = j0;
       advance();
-      if (sg < nseg) dma_kv(s, j0, sK1, sV1);
+      if (sg < nseg) dma_kv(s, j0, sK1, sV1, sK81);
       if (wave_active) {
         const bool need = cj0 + kBN > cs.n_full;
         const int lim = min(cs.n_hi - 1, bound - cs.cpos0) - cj0 - 4 * hf;
-        dq_block(acc, qreg, dreg, sK0, sV0, need, lim, lse2, ndelta, c, no, to);
+        dq_block<QK8>(acc, qreg, q8, dreg, sK0, sK80, sV0, need, lim, lse2, ndelta, c, no, no8, to);
       }
       dma_wait();
       __syncthreads();
@@ -180,11 +217,11 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bwd_dq_bf16_kernel(BwdDqArgs
       const Seg cs = s;
       const int cj0 = j0;
       advance();
-      if (sg < nseg) dma_kv(s, j0, sK0, sV0);
+      if (sg < nseg) dma_kv(s, j0, sK0, sV0, sK80);
       if (wave_active) {
         const bool need = cj0 + kBN > cs.n_full;
         const int lim = min(cs.n_hi - 1, bound - cs.cpos0) - cj0 - 4 * hf;
-        dq_block(acc, qreg, dreg, sK1, sV1, need, lim, lse2, ndelta, c, no, to);
+        dq_block<QK8>(acc, qreg, q8, dreg, sK1, sK81, sV1, need, lim, lse2, ndelta, c, no, no8, to);
       }
       dma_wait();
       __syncthreads();
@@ -532,17 +569,26 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16_kernel(BwdDkdvArgs a) {
     }
 }
 
-template __global__ void bwd_dq_bf16_kernel<false>(BwdDqArgs);
-template __global__ void bwd_dq_bf16_kernel<true>(BwdDqArgs);
+template __global__ void bwd_dq_bf16_kernel<false, false>(BwdDqArgs);
+template __global__ void bwd_dq_bf16_kernel<true, false>(BwdDqArgs);
+template __global__ void bwd_dq_bf16_kernel<false, true>(BwdDqArgs);
+template __global__ void bwd_dq_bf16_kernel<true, true>(BwdDqArgs);
 
 }  // namespace
 
 hipError_t launch_bwd_dq_bf16(const BwdDqArgs &a, int n_tiles, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
-  if (a.runs)
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<true>), dim3(n_tiles), dim3(kDqWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<false>), dim3(n_tiles), dim3(kDqWaves * 64), 0, s, a);
+  const dim3 g(n_tiles), b(kDqWaves * 64);
+  if (a.k8 != nullptr) {
+    if (a.runs)
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, true>), g, b, 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, true>), g, b, 0, s, a);
+  } else if (a.runs) {
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<true, false>), g, b, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<false, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 

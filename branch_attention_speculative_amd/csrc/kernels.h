@@ -64,6 +64,9 @@ struct BwdBranchArgs {
 // Ring replay for dQ (query-stationary).
 struct BwdDqArgs {
   const void *q, *qb, *k, *v, *dout, *doutb;
+  // fp8 plans: the E4M3 q, qb, k for the scores (q/qb/k above are then their
+  // exact bf16 copies, used for the K^T dS^T product); NULL otherwise
+  const void *q8, *qb8, *k8;
   const float *lse, *lseb, *ndelta;  // -Delta: main rows then branch rows
   const float *lse2;                // LSE * log2(e), main rows then branch rows
   const float *dq_local;            // branch rows: branch-key share of dQ

@@ -348,4 +348,61 @@ __device__ __forceinline__ void lds_zero(u16 *p, int n, int tid, int nthreads) {
   for (int i = 8 * tid; i < n; i += 8 * nthreads) *reinterpret_cast<u32x4 *>(p + i) = u32x4{0, 0, 0, 0};
 }
 
+// ---- fp8 (OCP E4M3) operands -------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---- fp8 K tile layout ------------------------------------------------------
+// 64 key rows x 128 fp8 bytes, no padding; logical 16-byte chunk c of row r
+// sits at physical chunk c ^ swz8(r), swz8(r) = (r >> 1) & 7. Rows are 128
+// bytes (half the 256-byte bank sweep), so the 16 lanes of a quarter wave
+// that read one chunk of 16 consecutive rows hit bank groups
+// 8 (r & 1) + (c ^ swz8(r)): the even rows fill groups 0..7 and the odd rows
+// 8..15, each exactly once.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+// 32x32x64 fp8 (E4M3) x fp8 matrix-core product, fp32 accumulate. Operand
+// lane layout (lane l, i = l % 32, h = l / 32): A (32 x 64): A[i][32h .. 32h+31];
+// B (64 x 32): B[32h .. 32h+31][i]; C as for mfma32.
+__device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Byte offsets of this lane's two 16-byte reads of the A operand for key
+// rows 0..31 and D step kk (bytes 64 kk + 32 h .. + 31): add 32 * 128 for
+// key rows 32..63.
+struct Nat8Off {
+  int o[2][2];
+};
+__device__ __forceinline__ Nat8Off nat8_offsets(int lane) {
+  const int i = lane & 31, h = lane >> 5;
+  Nat8Off r;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) r.o[kk][t] = 128 * i + 16 * ((4 * kk + 2 * h + t) ^ swz8(i));
+  return r;
+}
+__device__ __forceinline__ i32x8 lds_nat8(const u16 *X, int row0, int kk, const Nat8Off &no) {
+  const char *b = reinterpret_cast<const char *>(X) + 128 * row0;
+  const u32x4 lo = *reinterpret_cast<const u32x4 *>(b + no.o[kk][0]);
+  const u32x4 hi = *reinterpret_cast<const u32x4 *>(b + no.o[kk][1]);
+  return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+               int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+}
+
+// Direct global -> LDS load of a 64-row fp8 K tile: 8 KB, one 1 KB
+// instruction per wave of the 8. Instruction J fills rows 8J .. 8J + 7; its
+// lane i writes physical chunk i % 8 of row 8J + i / 8, i.e. logical chunk
+// (i % 8) ^ swz8(row). rowstride: bytes between key rows in global memory.
+__device__ __forceinline__ uint32_t dma8_offset(int wave, int lane, int64_t rowstride) {
+  const int row = 8 * wave + (lane >> 3);
+  const int c = (lane & 7) ^ swz8(row);
+  return uint32_t(int64_t(row) * rowstride + 16 * c);
+}
+__device__ __forceinline__ void dma_tile64_f8(u16 *lds_tile, __amdgpu_buffer_rsrc_t rs,
+                                              uint32_t off, int wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(reinterpret_cast<char *>(lds_tile) + 1024 * wave),
+                                           16, off, 0, 0, 0);
+}
+
 }  // namespace ba

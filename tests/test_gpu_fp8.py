@@ -4,9 +4,11 @@ decoded fp8 values. The pages name fp8 as a precision to watch for the
 online-softmax merge (rainbus analysis, weaknesses and improvements, item 4);
 the tolerances are the bf16 ones: O max-abs <= 2e-2 and rel-L2 <= 1e-2, LSE
 max-abs <= 1e-3, gradients as for bf16 inputs. The backward takes the E4M3
-values as bf16 and runs the bf16 backward, which one test checks bit for bit
-against the bf16 plan on the decoded values. The inputs are the bf16
-workloads' seeded N(0, 1) draws, encoded to E4M3 for the score operands."""
+values as bf16 and runs the bf16 backward, except that the dQ kernel forms
+the scores on the fp8 matrix cores; one test checks it against the bf16 plan
+on the decoded values: dK, dV, dKb, dVb bit for bit, dQ and dQb to a
+rounding-order bound. The inputs are the bf16 workloads' seeded N(0, 1)
+draws, encoded to E4M3 for the score operands."""
 
 
 import numpy as np
@@ -163,7 +165,13 @@ def _fwd_bwd_against_oracle(env, w):
 def test_fp8_backward_equals_the_bf16_backward_on_decoded_values(env):
     """Every E4M3 value is a bf16 value: the fp8 plan's backward and the bf16
     plan's backward on q, k, qb, kb decoded to bf16 (same O, LSE and dO) give
-    identical gradients."""
+    identical dK, dV, dKb, dVb. dQ and dQb differ only in the fp32 rounding
+    order of the scores in the dQ kernel (fp8 products summed 64 at a time
+    against 16). That moves P by a few fp32 steps, which can move a dS
+    element across a bf16 rounding boundary before the dS K product, so
+    single dQ elements may move by a few bf16 steps of their larger terms.
+    The bound: the bf16 gradient one (max-abs <= 2e-2 * max(1, |dQ|_inf)) and
+    relative L2 <= 2e-3 (about 4e-4 measured on this workload)."""
     torch, ba = env
     w8 = _fp8(workloads.make("long256k_r"))
     w16 = workloads.make("long256k_r")
@@ -179,5 +187,13 @@ def test_fp8_backward_equals_the_bf16_backward_on_decoded_values(env):
                  lseb, dev["do"], dev["dob"])
     torch.cuda.synchronize()
     for nm, a, b in zip(("dq", "dk", "dv", "dqb", "dkb", "dvb"), g8, g16):
-        assert torch.equal(a, b), nm
-    say(f"  fp8 and bf16 backward bit-identical on {N} rows + {NB} branch rows")
+        if nm in ("dq", "dqb"):
+            a, b = to_host(a).astype(np.float64), to_host(b).astype(np.float64)
+            d = np.abs(a - b)
+            rl = rel_l2(a, b)
+            say(f"  {nm}: {np.count_nonzero(d)} of {d.size} differ, max {d.max():.3e}, "
+                f"relL2 {rl:.3e}")
+            assert rl <= 2e-3 and d.max() <= 2e-2 * max(1.0, np.max(np.abs(b))), (nm, rl, d.max())
+        else:
+            assert torch.equal(a, b), nm
+    say(f"  fp8 and bf16 backward agree on {N} rows + {NB} branch rows")
