@@ -41,3 +41,24 @@ def test_bench_prints_one_complete_json_line():
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1 and c["sample"]
     p = d["mfma_probe"]
     assert p["zero_operands_tflops"] > 0 and p["random_operands_tflops"] > 0
+
+
+def test_bench_fp8_step_with_the_backward():
+    """--dtype fp8 --fp8-step fwd+bwd on the ttt32k workload: the
+    backward runs (its kernels in the per-kernel table), the metric and peak
+    are the fp8 step's, and the dominant kernel is priced at its own peak."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() < 1:
+        pytest.skip("no GPU visible")
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "ttt32k",
+                          "--dtype", "fp8", "--fp8-step", "fwd+bwd", "--steps", "2", "--warmup", "1",
+                          "--cpu-anchors", "0", "--mfma-probe-iters", "0"],
+                         capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    d = json.loads([l for l in res.stdout.splitlines() if l.strip()][-1])
+    assert d["dtype"] == "fp8" and "fwd+bwd" in d["metric"]
+    assert {"fwd_ring", "bwd_dq", "bwd_dkdv"} <= set(d["kernels"])
+    assert d["split"]["bwd_ms"] > 0
+    assert 2516.6 < 100.0 * d["value"] / d["pct_of_peak"] < 5033.2
+    r = d["roofline"]
+    assert r["kernel"] == "bwd_dkdv" and r["peak"] == 2516.6 and r["traffic"] is None
