@@ -11,6 +11,7 @@ The rel-L2 guard on O matters at long context, where |O| itself shrinks
 towards 2e-2 and a max-abs bound alone would accept O = 0.
 """
 
+import dataclasses
 import time
 
 import numpy as np
@@ -537,15 +538,20 @@ def test_element_offsets_beyond_2_31(env):
     assert ev <= 1e-2 and ek <= 1e-2
 
 
-@pytest.mark.parametrize("name", ["ttt32k", "dflash", "dspark", "long256k"])
+@pytest.mark.parametrize("name", ["ttt32k", "dflash", "dspark", "long256k", "long256k-fp8"])
 def test_full_size_sampled(env, name):
     """Full-size workloads: the first and last 64 rows of every local chunk
     (and random rows and anchors) against the oracle's dense form of that row
     subset; dK/dV element by element on every key whose viewers are all in the
     subset (at long256k: the last 64 keys of the sequence); the gradient sum
-    rules over the whole tensors."""
+    rules over the whole tensors. long256k-fp8 is the same share with E4M3
+    q, k, qb, kb (the fp8 plan's forward and backward kernels), against the
+    oracle on the decoded values."""
     torch, ba = env
-    w = workloads.make(name)
+    base = name[:-4] if name.endswith("-fp8") else name
+    w = workloads.make(base)
+    if name.endswith("-fp8"):
+        w = dataclasses.replace(w, name=name, dtype="fp8")
     say(f"[case] full-size {name}")
     lay, br = oracle_structs(w)
     plan = make_plan(ba, w)
