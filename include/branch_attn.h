@@ -84,7 +84,9 @@ typedef enum {
  * factors of Q and K fold into the softmax scale (s = scale * <q, k>). The
  * backward takes the E4M3 values of q, k, qb, kb as bf16 (each E4M3 value is
  * a bf16 value; the copies live in the backward workspace) and runs the bf16
- * backward: dq, dk, dqb, dkb are bf16 gradients with respect to those
+ * backward, except that the ring dQ kernel forms its scores by fp8 products
+ * of the E4M3 codes (the same products as the forward, summed in another
+ * order): dq, dk, dqb, dkb are bf16 gradients with respect to those
  * values. */
 typedef enum { BA_BF16 = 0, BA_FP32 = 1, BA_FP8 = 2 } ba_dtype;
 
