@@ -67,7 +67,7 @@ def _run(env, w, with_bwd, oracle_dtype=np.float32, prep=None, threads=4, walk=N
 
 
 def _check_fwd(w, got, ref):
-    bf16 = w.dtype == "bf16"
+    bf16 = w.dtype in ("bf16", "fp8")  # fp8 plans keep the bf16 bounds
     for o_name, l_name in (("o", "lse"), ("ob", "lseb")):
         if ref[o_name].size == 0:
             continue
@@ -85,7 +85,7 @@ def _check_fwd(w, got, ref):
 
 def _check_bwd(w, got, ref):
     for name in ("dq", "dk", "dv", "dqb", "dkb", "dvb"):
-        ok, ma, rl = grad_ok(got[name], ref[name], w.dtype == "bf16")
+        ok, ma, rl = grad_ok(got[name], ref[name], w.dtype in ("bf16", "fp8"))
         say(f"  {name}: max-abs={ma:.3e} relL2={rl:.3e} |ref|inf={np.max(np.abs(ref[name])) if ref[name].size else 0:.3e}")
         assert ok, (name, ma, rl)
 
@@ -235,6 +235,21 @@ def test_both_key_walks(env, name, walk):
     w = workloads.make(name) if name.endswith("_r") else next(e for e in EDGES if e.name == name)
     w = workloads.Workload(w.name, w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.hq, w.hkv, w.d,
                            w.dtype, True, w.seed, anchors=w.anchors, branch_lens=w.branch_lens)
+    got, ref, plan = _run(env, w, with_bwd=True, walk=walk)
+    assert plan.info["run_walk"] == (1 if walk == "runs" else 0)
+    _check_fwd(w, got, ref)
+    _check_bwd(w, got, ref)
+
+
+@pytest.mark.parametrize("walk", ["segments", "runs"])
+@pytest.mark.parametrize("name", ["ttt32k_r", "dspark_r", "long256k_r", "ragged"])
+def test_both_key_walks_fp8(env, name, walk):
+    """The same with E4M3 q, k, qb, kb: the fp8 instances of the forward and
+    dQ kernels on both walks, against the oracle on the decoded values."""
+    w = workloads.make(name) if name.endswith("_r") else next(e for e in EDGES if e.name == name)
+    w = workloads.Workload(w.name + "-fp8", w.seqlens, w.C, w.r, w.kind, w.depth_or_block, w.hq,
+                           w.hkv, w.d, "fp8", True, w.seed, anchors=w.anchors,
+                           branch_lens=w.branch_lens)
     got, ref, plan = _run(env, w, with_bwd=True, walk=walk)
     assert plan.info["run_walk"] == (1 if walk == "runs" else 0)
     _check_fwd(w, got, ref)
