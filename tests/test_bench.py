@@ -70,3 +70,15 @@ def test_cpu_baseline_on_the_tiny_workload():
     sampled, total = int(m.group(1)), int(m.group(2))
     assert total == counts["total"] and 0 < sampled < total
     assert out["extrapolated_step_s"] == pytest.approx(out["seconds"] * total / sampled)
+
+
+def test_blended_peaks():
+    """The fp8 forward's peak weighs Q K^T (fp8) and P V (bf16) equally; the
+    fp8 step's counts 4 of its 14 D per pair at the fp8 rate: the time of a
+    FLOP-weighted mix at each unit's own peak."""
+    fp8, bf16 = bench.PEAK_FP8_TFLOPS, bench.PEAK_BF16_TFLOPS
+    assert fp8 == pytest.approx(2 * bf16)
+    assert bench.PEAK_FP8_QK_BF16_PV_TFLOPS == pytest.approx(4 * bf16 / 3)
+    # 4 units at twice the rate and 10 at the base rate take 12 base-rate units
+    assert bench.PEAK_FP8_STEP_TFLOPS == pytest.approx(14 * bf16 / 12)
+    assert bench.PEAK_BF16_TFLOPS < bench.PEAK_FP8_STEP_TFLOPS < bench.PEAK_FP8_QK_BF16_PV_TFLOPS
